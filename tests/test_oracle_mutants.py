@@ -1,0 +1,183 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant is a copy of an oracle module's source with one plausible slip
+(an excluded diagonal, a reversed mask, log2 instead of ln, a flipped sign, a
+dropped scale, a missing normalization, a wrong GQA head map, an unrescaled
+denominator, an averaged merge, a dropped empty identity). The mutant runs in
+a private module object; the real oracle is never modified. A battery of pin
+checks -- hand-derived cases, closed forms and independent library routines --
+must reject every mutant.
+"""
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle.dense
+import oracle.online
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = json.load(open(os.path.join(HERE, "golden", "hand_derived_cases.json")))
+
+
+def _mutant(module, old, new, count=1):
+    src = open(module.__file__).read()
+    assert src.count(old) >= count, "mutation anchor not found: %r" % old
+    mod = types.ModuleType(module.__name__ + "_mutant")
+    mod.__file__ = module.__file__
+    exec(compile(src.replace(old, new), module.__file__, "exec"), mod.__dict__)
+    return mod
+
+
+# ---------------------------------------------------------- dense battery
+def _dense_checks(d):
+    """Yield (name, passed) for each pin applied to dense-oracle module d."""
+    def golden():
+        for case in GOLDEN["attention"]:
+            q, k, v = (np.array(case[x], dtype=np.float64) for x in ("q", "k", "v"))
+            for mode in ("noncausal", "causal"):
+                if mode in case:
+                    o, lse = d.attention(q, k, v, case["scale"], causal=(mode == "causal"))
+                    if not (np.allclose(o, case[mode]["o"], rtol=1e-12, atol=1e-12)
+                            and np.allclose(lse, case[mode]["lse"], rtol=1e-13, atol=1e-12)):
+                        return False
+        for case in GOLDEN["merge"]:
+            m = np.array([float(x) for x in case["m"]])
+            o, lse = d.merge_partials(m[None], np.array(case["l"])[None], np.array(case["acc"])[None])
+            want = float(case["lse"])
+            if np.isnan(o).any() or not np.allclose(o[0], case["o"], atol=1e-13):
+                return False
+            if (math.isinf(want) and lse[0] != want) or (not math.isinf(want) and abs(lse[0] - want) > 1e-13):
+                return False
+        return True
+
+    def sdpa():
+        rng = np.random.default_rng(1)
+        for causal in (False, True):
+            q, k, v = (rng.standard_normal((9, 4)) for _ in range(3))
+            o, lse = d.attention(q, k, v, 0.5, causal)
+            qt, kt, vt = (torch.from_numpy(x)[None] for x in (q, k, v))
+            o_ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=0.5)[0].numpy()
+            if not np.allclose(o, o_ref, rtol=1e-12, atol=1e-12):
+                return False
+        return True
+
+    def gqa():
+        rng = np.random.default_rng(2)
+        t, hq, hkv, dd = 7, 4, 2, 3
+        q = rng.standard_normal((t, hq, dd))
+        k = rng.standard_normal((t, hkv, dd))
+        v = rng.standard_normal((t, hkv, dd))
+        o, _ = d.varlen_gqa(q, k, v, np.array([0, t]), 0.5, causal=True)
+        qt, kt, vt = (torch.from_numpy(x).permute(1, 0, 2)[None] for x in (q, k, v))
+        o_ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=0.5,
+                                               enable_gqa=True)[0].permute(1, 0, 2).numpy()
+        return np.allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+
+    def split():
+        rng = np.random.default_rng(3)
+        q = rng.standard_normal((2, 4)) * 3
+        k = rng.standard_normal((21, 4))
+        v = rng.standard_normal((21, 4))
+        o, lse = d.merge_partials(*d.split_partials(q, k, v, 0.5, 8))
+        qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+        o_ref = F.scaled_dot_product_attention(qt[None], kt[None], vt[None], scale=0.5)[0].numpy()
+        lse_ref = torch.logsumexp(0.5 * qt @ kt.T, dim=-1).numpy()
+        return np.allclose(o, o_ref, rtol=1e-12, atol=1e-12) and np.allclose(lse, lse_ref, rtol=1e-12)
+
+    for name, fn in (("golden", golden), ("sdpa", sdpa), ("gqa", gqa), ("split", split)):
+        try:
+            ok = bool(fn())
+        except Exception:
+            ok = False
+        yield name, ok
+
+
+DENSE_MUTANTS = [
+    ("diagonal excluded", "key_idx[None, :] <= q_pos", "key_idx[None, :] < q_pos"),
+    ("mask reversed", "key_idx[None, :] <= q_pos", "key_idx[None, :] >= q_pos"),
+    ("log2 lse", "lse_blk = m_safe + np.log(", "lse_blk = m_safe + np.log2("),
+    ("max shift sign", "p = np.exp(s - m_safe[:, None])", "p = np.exp(s + m_safe[:, None])"),
+    ("scale dropped", "s = scale * (q[r0:r1] @ k.T)", "s = (q[r0:r1] @ k.T)"),
+    ("no normalization", "o_blk = num / np.where", "o_blk = num * 0 + num / 1 + 0 * np.where"),
+    ("gqa head map h % hkv", "g = h // group", "g = h % hkv", ),
+    ("merge weight sign", "np.exp(m - m0[..., None])", "np.exp(m0[..., None] - m)"),
+    ("merge denominator unrescaled", "big_l = (w * l).sum(axis=-1)", "big_l = l.sum(axis=-1)"),
+    ("merge averages outputs", "o = num / np.where(nonempty, big_l, 1.0)[..., None]",
+     "o = (acc / np.where(l > 0, l, 1.0)[..., None]).mean(axis=-2)"),
+    ("partial unshifted", "p = np.exp(s - m[:, c:c + 1])", "p = np.exp(s)"),
+    ("partial numerator without weights", "acc[:, c, :] = p @ v[j0:j1]", "acc[:, c, :] = v[j0:j1].sum(axis=0)"),
+]
+
+
+def test_real_dense_oracle_passes_battery():
+    assert all(ok for _, ok in _dense_checks(oracle.dense))
+
+
+@pytest.mark.parametrize("name,old,new", DENSE_MUTANTS, ids=[m[0] for m in DENSE_MUTANTS])
+def test_dense_mutant_is_caught(name, old, new):
+    mod = _mutant(oracle.dense, old, new)
+    results = dict(_dense_checks(mod))
+    assert not all(results.values()), "mutant '%s' survived every pin: %s" % (name, results)
+
+
+# --------------------------------------------------------- online battery
+def _online_checks(o):
+    def closed():
+        st = o.merge(o.block([0.0], [[3.0]], 1), o.block([math.log(2.0)], [[6.0]], 1))
+        out, lse = o.finalize(st)
+        return abs(out[0] - 5.0) < 1e-14 and abs(lse - math.log(3.0)) < 1e-14
+
+    def empties():
+        e = o.empty(2)
+        ee = o.merge(e, e)
+        out, lse = o.finalize(ee)
+        return lse == -math.inf and all(x == 0.0 for x in out) and not any(math.isnan(x) for x in ee[2]) \
+            and not math.isnan(ee[1])
+
+    def vs_logsumexp():
+        rng = np.random.default_rng(4)
+        s = (rng.standard_normal(30) * 4).tolist()
+        vals = rng.standard_normal((30, 2)).tolist()
+        st = o.fold([o.block(s[a:a + 7], vals[a:a + 7], 2) for a in range(0, 30, 7)], 2)
+        _, lse = o.finalize(st)
+        return abs(lse - float(torch.logsumexp(torch.tensor(s, dtype=torch.float64), 0))) < 1e-12
+
+    def large_logits():
+        st = o.merge(o.block([0.0], [[1.0]], 1), o.block([1000.0], [[2.0]], 1))
+        out, lse = o.finalize(st)
+        return abs(out[0] - 2.0) < 1e-12 and abs(lse - 1000.0) < 1e-12
+
+    for name, fn in (("closed", closed), ("empties", empties), ("logsumexp", vs_logsumexp),
+                     ("large", large_logits)):
+        try:
+            ok = bool(fn())
+        except Exception:
+            ok = False
+        yield name, ok
+
+
+ONLINE_MUTANTS = [
+    ("denominator not rescaled", "l = a[1] * fa + b[1] * fb", "l = a[1] + b[1]"),
+    ("numerator not rescaled", "acc = tuple(x * fa + y * fb for", "acc = tuple(x + y for"),
+    ("no explicit empty identity", "    if is_empty(a):\n        return b\n    if is_empty(b):\n        return a\n", ""),
+    ("log2 lse", "return tuple(x / l for x in acc), m + math.log(l)",
+     "return tuple(x / l for x in acc), m + math.log2(l)"),
+    ("max kept from first operand", "m = a[0] if a[0] >= b[0] else b[0]", "m = a[0]"),
+]
+
+
+def test_real_online_passes_battery():
+    assert all(ok for _, ok in _online_checks(oracle.online))
+
+
+@pytest.mark.parametrize("name,old,new", ONLINE_MUTANTS, ids=[m[0] for m in ONLINE_MUTANTS])
+def test_online_mutant_is_caught(name, old, new):
+    mod = _mutant(oracle.online, old, new)
+    results = dict(_online_checks(mod))
+    assert not all(results.values()), "mutant '%s' survived every pin: %s" % (name, results)

@@ -1,0 +1,402 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the exact streaming attention forward on one MI355X.
+
+One step = the batched multi-head forward B=4, H=16, N=4096, D=128 in bf16,
+run once noncausal and once causal on the same resident inputs. FLOPs are
+counted per head as 4*N^2*D noncausal and 2*N^2*D causal; ``value`` is the
+step's FLOPs over its wall time (TFLOP/s).
+
+Method, after the pages' timing rules ("Intermediate and advanced extension",
+code review and execution gates 5; "Intermediate and advanced workshop
+validation", measured examples): a correctness gate against the FP64 oracle
+before timing, untimed warmup steps, then timed steps between device
+synchronizations, with a HIP event pair around every launch on the stream the
+kernel runs on. Small shapes are timed separately as graph replays (20 calls
+captured in one HIP graph) and as eager event timing.
+
+Output: one JSON line on stdout (progress goes to stderr).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak; µs latency at N,D=512×64"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SOURCES = ["exact_tiled_attention_sattn_amd/csrc/fwd_kernel.hpp",
+                  "exact_tiled_attention_sattn_amd/csrc/common.hpp",
+                  "exact_tiled_attention_sattn_amd/csrc/sattn.hip"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_kernel_batched_4x16x4096x128_bf16_pmc.json")
+DEV = "cuda:0"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def dense_flops(b, h, n, d, causal):
+    return (2 if causal else 4) * b * h * n * n * d
+
+
+def gate_dense(fwd, q, k, v, scale, causal, rows_per_head, seed, dtype):
+    """Correctness gate: sampled rows against the FP64 oracle."""
+    from oracle import dense
+    from tests.parity import check_attention
+    b, h, n, d = q.shape
+    o, lse = fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = W.sample_rows(seed, n, rows_per_head, groups=b * h).reshape(b, h, -1)
+    qh, kh, vh = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    o_ref, lse_ref = dense.attention_bhnd(qh, kh, vh, scale, causal, rows=rows)
+    idx = torch.from_numpy(rows)
+    oc, lc = o.cpu(), lse.cpu()
+    o_s = torch.stack([torch.stack([oc[i, j][idx[i, j]] for j in range(h)]) for i in range(b)])
+    l_s = torch.stack([torch.stack([lc[i, j][idx[i, j]] for j in range(h)]) for i in range(b)])
+    return check_attention(o_s, l_s, o_ref, lse_ref, dtype, "gate")
+
+
+def time_launches(fn, steps, warmup):
+    """Per-launch HIP events on the current stream; returns list of ms."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def graph_latency_us(fn, calls=20, samples=7, warmup=5):
+    """Median per-call latency of ``calls`` launches captured in one graph."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fn()  # warm on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(calls):
+                fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(samples):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) * 1000.0 / calls)
+    return out
+
+
+def event_latency_us(fn, calls=20, samples=7, warmup=5):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(samples):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(calls):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) * 1000.0 / calls)
+    return out
+
+
+def small_latency(fwd, n, d, dtype_name, seed, causal, qmul=1.0):
+    q, k, v = W.qkv((1, 1, n, d), (1, 1, n, d), dtype_name, seed)
+    if qmul != 1.0:
+        q = (q.float() * qmul).to(q.dtype)
+    q, k, v = (x.to(DEV) for x in (q, k, v))
+    scale = W.scale_f32(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, n), dtype=torch.float32, device=DEV)
+    fn = lambda: fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)  # noqa: E731
+    # gate against the oracle (full)
+    from oracle import dense
+    from tests.parity import check_attention
+    fn()
+    torch.cuda.synchronize()
+    o_ref, l_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o, lse, o_ref, l_ref, W.DTYPES[dtype_name], "gate %dx%d" % (n, d))
+    gr = graph_latency_us(fn)
+    ev = event_latency_us(fn)
+    return {"graph_us_median": float(np.median(gr)), "graph_us_min": float(min(gr)), "graph_us_max": float(max(gr)),
+            "event_us_median": float(np.median(ev)), "graph_samples_us": gr, "event_samples_us": ev}
+
+
+def decode_extra(steps):
+    """Split-KV decode B=16, Hq=Hkv=32, Nk=131072, D=128, chunks of 4096."""
+    from exact_tiled_attention_sattn_amd import sattn_fwd_split, sattn_merge
+    cfg = W.WORKLOADS["splitkv_decode_16x32x131072x128_bf16"]
+    b, hq, hkv, nk, d, chunk = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Nk"], cfg["D"], cfg["chunk"]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(cfg["seed"])
+    q = W.randn_device_sliced((b, hq, 1, d), "bf16", g, DEV)
+    k = W.randn_device_sliced((b, hkv, nk, d), "bf16", g, DEV)
+    v = W.randn_device_sliced((b, hkv, nk, d), "bf16", g, DEV)
+    c = -(-nk // chunk)
+    pm = torch.empty((b, hq, 1, c), dtype=torch.float32, device=DEV)
+    pl = torch.empty_like(pm)
+    pa = torch.empty((b, hq, 1, c, d), dtype=torch.float32, device=DEV)
+    o = torch.empty((b, hq, 1, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((b, hq, 1), dtype=torch.float32, device=DEV)
+    scale = W.scale_f32(d)
+    split = lambda: sattn_fwd_split(q, k, v, chunk, scale, part_m=pm, part_l=pl, part_acc=pa)  # noqa: E731
+    merge = lambda: sattn_merge(pm, pl, pa, torch.bfloat16, out=o, lse=lse)  # noqa: E731
+    # gate: 4 rows against the oracle
+    from oracle import dense
+    from tests.parity import check_attention
+    split()
+    merge()
+    torch.cuda.synchronize()
+    for flat in (0, 137, 300, 511):
+        bb, h = divmod(flat, hq)
+        o_ref, l_ref = dense.attention(W.to_f64(q[bb, h]), W.to_f64(k[bb, h]), W.to_f64(v[bb, h]), scale)
+        check_attention(o[bb, h], lse[bb, h], o_ref, l_ref, torch.bfloat16, "gate decode")
+    t_split = time_launches(split, steps, 2)
+    t_merge = time_launches(merge, steps, 2)
+    kv_bytes = 2 * b * hkv * nk * d * 2
+    part_bytes = b * hq * c * (d + 2) * 4
+    io_bytes = b * hq * d * 2 * 2 + b * hq * 4
+    split_bytes = kv_bytes + b * hq * d * 2 + part_bytes
+    merge_bytes = part_bytes + b * hq * d * 2 + b * hq * 4
+    ms_split, ms_merge = float(np.mean(t_split)), float(np.mean(t_merge))
+    total_bytes = kv_bytes + 2 * part_bytes + io_bytes
+    out = {"workload": "splitkv_decode_16x32x131072x128_bf16 (chunk 4096, 32 partials per row)",
+           "split_ms_mean": ms_split, "merge_ms_mean": ms_merge,
+           "split_GBps": split_bytes / ms_split / 1e6, "merge_GBps": merge_bytes / ms_merge / 1e6,
+           "end_to_end_GBps": total_bytes / (ms_split + ms_merge) / 1e6,
+           "split_frac_of_hbm_peak": split_bytes / ms_split / 1e6 / PEAK_HBM_GBS,
+           "algorithmic_bytes_split": split_bytes, "algorithmic_bytes_merge": merge_bytes}
+    del q, k, v
+    torch.cuda.empty_cache()
+    return out
+
+
+def varlen_extra(steps):
+    from exact_tiled_attention_sattn_amd import sattn_fwd_varlen
+    cfg = W.WORKLOADS["varlen_gqa_8seq_32q8kv_128_bf16_causal"]
+    lengths = W.varlen_lengths(cfg["seed"], cfg["S"], cfg["max_len"])
+    hq, hkv, d = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    t = int(lengths.sum())
+    q, k, v = W.qkv((t, hq, d), (t, hkv, d), "bf16", cfg["seed"])
+    q, k, v = (x.to(DEV) for x in (q, k, v))
+    cu = torch.from_numpy(W.cu_seqlens_of(lengths)).to(DEV)
+    mx = int(lengths.max())
+    scale = W.scale_f32(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, t), dtype=torch.float32, device=DEV)
+    fn = lambda: sattn_fwd_varlen(q, k, v, cu, max_seqlen=mx, causal=True, scale=scale, out=o, lse=lse)  # noqa
+    ms = float(np.mean(time_launches(fn, steps, 2)))
+    flops = sum(2 * int(L) * int(L) * d * hq for L in lengths)
+    return {"workload": "varlen_gqa_8seq_32q8kv_128_bf16_causal", "lengths": lengths.tolist(), "T": t,
+            "ms_mean": ms, "TFLOPs": flops / ms / 1e9, "frac_of_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "flop": flops}
+
+
+def cpu_baseline(budget_s):
+    """The FP64 oracle on sampled query rows of the batched workload, both
+    variants, on the host cores, scaled to TFLOP/s by the sampled fraction."""
+    from oracle import dense
+    b, h, n, d = 4, 16, 4096, 128
+    q, k, v = W.qkv((b, h, n, d), (b, h, n, d), "bf16", W.WORKLOADS["batched_4x16x4096x128_bf16"]["seed"])
+    qh, kh, vh = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    scale = W.scale_f32(d)
+    rows_done = 0
+    t0 = time.perf_counter()
+    per = 64
+    heads_done = 0
+    while True:
+        bh = heads_done % (b * h)
+        bi, hi = divmod(bh, h)
+        r = W.sample_rows(1000 + heads_done, n, per)[0]
+        for causal in (False, True):
+            dense.attention(qh[bi, hi][r], kh[bi, hi], vh[bi, hi], scale, causal, q_pos=r)
+        rows_done += per
+        heads_done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    frac = rows_done / float(b * h * n)     # fraction of all query rows, both variants each
+    step_flop = dense_flops(b, h, n, d, False) + dense_flops(b, h, n, d, True)
+    value = frac * step_flop / el / 1e12
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "numpy float64 dense oracle on %d sampled query rows (64 per head, both causal and noncausal "
+                      "variants, all 4096 keys) of the 4x16x4096x128 workload in %.1f s; scaled by the sampled "
+                      "fraction of rows (%.5f)" % (rows_done, el, frac),
+            "host_cores_visible": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
+
+
+def load_traffic(src_hash, launch_bytes):
+    """HBM traffic of the dominant kernel from the committed counter summary,
+    only if it was taken on the current kernel sources."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    try:
+        with open(PMC_SUMMARY) as fh:
+            s = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_source_sha256") != src_hash:
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-gate", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention path runs whole on a single MI355X "
+              "(sharding across GPUs is described in the design notes, not run). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    from exact_tiled_attention_sattn_amd import sattn_fwd, library
+    library()
+
+    # A plain copy of known size (the counter-scaling reference for --pmc runs).
+    cal = torch.empty(64 << 20, dtype=torch.float32, device=DEV)
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    torch.cuda.synchronize()
+    del cal, cal2
+
+    b, h, n, d = 4, 16, 4096, 128
+    seed = W.WORKLOADS["batched_4x16x4096x128_bf16"]["seed"]
+    log("generating inputs")
+    q, k, v = W.qkv((b, h, n, d), (b, h, n, d), "bf16", seed)
+    q, k, v = (x.to(DEV) for x in (q, k, v))
+    scale = W.scale_f32(d)
+    gates = {}
+    if not args.no_gate:
+        for causal in (False, True):
+            log("correctness gate causal=%s" % causal)
+            gates["causal" if causal else "noncausal"] = gate_dense(
+                sattn_fwd, q, k, v, scale, causal, 16, seed, torch.bfloat16)
+    o_nc = torch.empty_like(q)
+    o_c = torch.empty_like(q)
+    l_nc = torch.empty((b, h, n), dtype=torch.float32, device=DEV)
+    l_c = torch.empty_like(l_nc)
+
+    for _ in range(args.warmup):
+        sattn_fwd(q, k, v, causal=False, scale=scale, out=o_nc, lse=l_nc)
+        sattn_fwd(q, k, v, causal=True, scale=scale, out=o_c, lse=l_c)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        sattn_fwd(q, k, v, causal=False, scale=scale, out=o_nc, lse=l_nc)
+        e[1].record()
+        e[2].record()
+        sattn_fwd(q, k, v, causal=True, scale=scale, out=o_c, lse=l_c)
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_nc = [e[0].elapsed_time(e[1]) for e in ev]
+    ms_c = [e[2].elapsed_time(e[3]) for e in ev]
+    ms_step = wall * 1000.0 / args.steps
+    f_nc, f_c = dense_flops(b, h, n, d, False), dense_flops(b, h, n, d, True)
+    value = (f_nc + f_c) / (ms_step / 1000.0) / 1e12
+    tf_nc = f_nc / (np.mean(ms_nc) / 1000.0) / 1e12
+    tf_c = f_c / (np.mean(ms_c) / 1000.0) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash, None)
+    roofline = {"bound": "mfma", "achieved": tf_nc, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf_nc / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "kernel": "fwd_kernel<Bf16, D=128, BN=64, 4 waves, noncausal>",
+                "algorithmic_flop_per_launch": f_nc,
+                "launch_ms_mean": float(np.mean(ms_nc))}
+    extras = {"noncausal_TFLOPs": tf_nc, "causal_TFLOPs": tf_c,
+              "noncausal_frac_of_bf16_peak": tf_nc / PEAK_BF16_TFLOPS,
+              "causal_frac_of_bf16_peak": tf_c / PEAK_BF16_TFLOPS,
+              "noncausal_launch_ms": {"mean": float(np.mean(ms_nc)), "min": float(min(ms_nc)),
+                                      "max": float(max(ms_nc))},
+              "causal_launch_ms": {"mean": float(np.mean(ms_c)), "min": float(min(ms_c)), "max": float(max(ms_c))},
+              "gate": gates, "kernel_source_sha256": src_hash}
+    del q, k, v, o_nc, o_c
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        log("small-shape latency")
+        extras["latency_512x64_fp16_causal"] = small_latency(sattn_fwd, 512, 64, "fp16", 2, True)
+        extras["latency_512x64_fp16_noncausal"] = small_latency(sattn_fwd, 512, 64, "fp16", 2, False)
+        extras["latency_129x32_fp16_causal"] = small_latency(sattn_fwd, 129, 32, "fp16", 1, True)
+        log("split-KV decode")
+        extras["splitkv_decode"] = decode_extra(max(3, min(args.steps, 10)))
+        log("varlen GQA")
+        extras["varlen_gqa"] = varlen_extra(max(3, min(args.steps, 10)))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(args.cpu_budget_s)
+    line = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "batched_4x16x4096x128_bf16: one noncausal + one causal forward per step",
+                       "B": b, "H": h, "N": n, "D": d, "flop_per_step": f_nc + f_c,
+                       "flop_convention": "4*N^2*D per head noncausal, 2*N^2*D causal",
+                       "parallelism": "single GPU"},
+            "frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
+            "roofline": roofline, "cpu_baseline": cpu, "extras": extras}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

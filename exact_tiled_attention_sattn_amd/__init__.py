@@ -1,0 +1,252 @@
+"""Exact streaming attention forward for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libsattn.so`` (declared in
+``include/sattn.h``). The functions carry the C names and only marshal
+arguments: they check tensor dtype/device/shape/contiguity, allocate outputs
+with torch when the caller does not pass them, and hand raw device pointers
+and the current HIP stream to the library. Every step of the computation runs
+in the HIP kernels; there is no fallback. If the library is missing, every
+call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen",
+    "SattnError", "library", "LIB_PATH", "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsattn.so")
+
+STATUS = {
+    0: "SATTN_OK", 1: "SATTN_ERR_NULL", 2: "SATTN_ERR_SHAPE", 3: "SATTN_ERR_DTYPE",
+    4: "SATTN_ERR_UNSUPPORTED", 5: "SATTN_ERR_ALIGN", 6: "SATTN_ERR_ALIAS",
+    7: "SATTN_ERR_HIP", 8: "SATTN_ERR_VALUE",
+}
+_DTYPE_CODE = {torch.float16: 0, torch.bfloat16: 1}
+
+_lib = None
+
+
+class SattnError(RuntimeError):
+    """A libsattn call returned a non-OK status."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__("%s: %s" % (STATUS.get(status, "status %d" % status), detail))
+
+
+def library():
+    """Load libsattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsattn.so is not built (%s); run "
+                           "`python -m exact_tiled_attention_sattn_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, fp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+    lib.sattn_status_string.restype = ctypes.c_char_p
+    lib.sattn_status_string.argtypes = [i32]
+    lib.sattn_last_error.restype = ctypes.c_char_p
+    lib.sattn_last_error.argtypes = []
+    lib.sattn_fwd.restype = i32
+    lib.sattn_fwd.argtypes = [i32, vp, vp, vp, vp, fp, i64, i64, i64, i64, i32, ctypes.c_float, vp]
+    lib.sattn_fwd_split.restype = i32
+    lib.sattn_fwd_split.argtypes = [i32, vp, vp, vp, fp, fp, fp, i64, i64, i64, i64, i64, i64, i64,
+                                    ctypes.c_float, vp]
+    lib.sattn_merge.restype = i32
+    lib.sattn_merge.argtypes = [i32, fp, fp, fp, i64, i64, i64, vp, fp, vp]
+    lib.sattn_fwd_varlen.restype = i32
+    lib.sattn_fwd_varlen.argtypes = [i32, vp, vp, vp, vp, fp, vp, i64, i64, i64, i64, i64, i64, i32,
+                                     ctypes.c_float, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise SattnError(status, library().sattn_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts[1:]:
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on %s" % dev)
+    return dev
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def sattn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Attention forward on [B, H, N, D] tensors (fp16 or bf16).
+
+    Returns (o [B,H,N,D] in q's dtype, lse [B,H,N] float32)."""
+    lib = library()
+    _dev_tensor(q, "q", ndim=4)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q must be float16 or bfloat16")
+    _dev_tensor(k, "k", q.dtype, 4)
+    _dev_tensor(v, "v", q.dtype, 4)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share shape [B, H, N, D]")
+    dev = _same_device(q, k, v, out, lse)
+    b, h, n, d = q.shape
+    out = torch.empty_like(q) if out is None else _dev_tensor(out, "out", q.dtype, 4)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=dev) if lse is None else \
+        _dev_tensor(lse, "lse", torch.float32, 3)
+    if out.shape != q.shape or lse.shape != (b, h, n):
+        raise ValueError("out/lse shape mismatch")
+    with torch.cuda.device(dev):
+        _check(lib.sattn_fwd(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                             b, h, n, d, int(bool(causal)), _scale(scale, d), _stream(dev)))
+    return out, lse
+
+
+def split_num_chunks(nk, chunk):
+    return -(-nk // chunk)
+
+
+def sattn_fwd_split(q, k, v, chunk, scale=None, part_m=None, part_l=None, part_acc=None):
+    """Split-KV partial states (non-causal). q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D].
+
+    Returns (part_m [B,Hq,Nq,C], part_l [B,Hq,Nq,C], part_acc [B,Hq,Nq,C,D]),
+    all float32, acc not normalized."""
+    lib = library()
+    _dev_tensor(q, "q", ndim=4)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q must be float16 or bfloat16")
+    _dev_tensor(k, "k", q.dtype, 4)
+    _dev_tensor(v, "v", q.dtype, 4)
+    dev = _same_device(q, k, v, part_m, part_l, part_acc)
+    b, hq, nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != b or k.shape[3] != d:
+        raise ValueError("k/v must be [B, Hkv, Nk, D] matching q")
+    hkv, nk = k.shape[1], k.shape[2]
+    chunk = int(chunk)
+    if chunk <= 0:
+        raise ValueError("chunk must be > 0")
+    c = split_num_chunks(nk, chunk)
+    shp = (b, hq, nq, c)
+    f32 = torch.float32
+    part_m = torch.empty(shp, dtype=f32, device=dev) if part_m is None else _dev_tensor(part_m, "part_m", f32, 4)
+    part_l = torch.empty(shp, dtype=f32, device=dev) if part_l is None else _dev_tensor(part_l, "part_l", f32, 4)
+    part_acc = torch.empty(shp + (d,), dtype=f32, device=dev) if part_acc is None else \
+        _dev_tensor(part_acc, "part_acc", f32, 5)
+    if part_m.shape != shp or part_l.shape != shp or part_acc.shape != shp + (d,):
+        raise ValueError("partial buffer shape mismatch")
+    with torch.cuda.device(dev):
+        _check(lib.sattn_fwd_split(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(part_m), _ptr(part_l),
+                                   _ptr(part_acc), b, hq, hkv, nq, nk, d, chunk, _scale(scale, d),
+                                   _stream(dev)))
+    return part_m, part_l, part_acc
+
+
+def sattn_merge(part_m, part_l, part_acc, dtype, out=None, lse=None):
+    """Merge partial states [..., C] / [..., C, D] into (o [..., D] of
+    ``dtype``, lse [...] float32)."""
+    lib = library()
+    f32 = torch.float32
+    _dev_tensor(part_m, "part_m", f32)
+    _dev_tensor(part_l, "part_l", f32)
+    _dev_tensor(part_acc, "part_acc", f32)
+    if dtype not in _DTYPE_CODE:
+        raise ValueError("dtype must be float16 or bfloat16")
+    dev = _same_device(part_m, part_l, part_acc, out, lse)
+    lead = tuple(part_m.shape[:-1])
+    c = part_m.shape[-1]
+    d = part_acc.shape[-1]
+    if part_l.shape != part_m.shape or tuple(part_acc.shape[:-1]) != tuple(part_m.shape):
+        raise ValueError("partial buffer shape mismatch")
+    rows = int(math.prod(lead))
+    out = torch.empty(lead + (d,), dtype=dtype, device=dev) if out is None else _dev_tensor(out, "out", dtype)
+    lse = torch.empty(lead, dtype=f32, device=dev) if lse is None else _dev_tensor(lse, "lse", f32)
+    if tuple(out.shape) != lead + (d,) or tuple(lse.shape) != lead:
+        raise ValueError("out/lse shape mismatch")
+    with torch.cuda.device(dev):
+        _check(lib.sattn_merge(_DTYPE_CODE[dtype], _ptr(part_m), _ptr(part_l), _ptr(part_acc), rows, c, d,
+                               _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def check_cu_seqlens(cu, total, max_seqlen):
+    """Validate a host copy of cu_seqlens: cu[0] = 0, non-decreasing,
+    cu[-1] = T, every length <= max_seqlen. Raises ValueError."""
+    cu = [int(x) for x in cu]
+    if len(cu) < 1 or cu[0] != 0:
+        raise ValueError("cu_seqlens must start at 0")
+    for a, b in zip(cu[:-1], cu[1:]):
+        if b < a:
+            raise ValueError("cu_seqlens must be non-decreasing")
+        if b - a > max_seqlen:
+            raise ValueError("a sequence is longer than max_seqlen")
+    if cu[-1] != total:
+        raise ValueError("cu_seqlens[-1] must equal T")
+
+
+def sattn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=True, scale=None, out=None, lse=None):
+    """Packed variable-length GQA forward. q [T,Hq,D], k/v [T,Hkv,D];
+    cu_seqlens int32 [S+1] (host or device; validated on a host copy).
+
+    Returns (o [T,Hq,D], lse [Hq,T] float32)."""
+    lib = library()
+    _dev_tensor(q, "q", ndim=3)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q must be float16 or bfloat16")
+    _dev_tensor(k, "k", q.dtype, 3)
+    _dev_tensor(v, "v", q.dtype, 3)
+    dev = _same_device(q, k, v, out, lse)
+    t, hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != t or k.shape[2] != d:
+        raise ValueError("k/v must be [T, Hkv, D] matching q")
+    hkv = k.shape[1]
+    cu_host = cu_seqlens.detach().to("cpu", torch.int64) if isinstance(cu_seqlens, torch.Tensor) else \
+        torch.as_tensor(cu_seqlens, dtype=torch.int64)
+    lengths = (cu_host[1:] - cu_host[:-1]).tolist()
+    if max_seqlen is None:
+        max_seqlen = max(lengths) if lengths else 0
+    check_cu_seqlens(cu_host.tolist(), t, max_seqlen)
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32 \
+            and cu_seqlens.is_contiguous() and cu_seqlens.device == dev:
+        cu_dev = cu_seqlens
+    else:
+        cu_dev = cu_host.to(torch.int32).to(dev)
+    s = cu_dev.numel() - 1
+    out = torch.empty_like(q) if out is None else _dev_tensor(out, "out", q.dtype, 3)
+    lse = torch.empty((hq, t), dtype=torch.float32, device=dev) if lse is None else \
+        _dev_tensor(lse, "lse", torch.float32, 2)
+    if out.shape != q.shape or lse.shape != (hq, t):
+        raise ValueError("out/lse shape mismatch")
+    with torch.cuda.device(dev):
+        _check(lib.sattn_fwd_varlen(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                    _ptr(cu_dev), s, t, int(max_seqlen), hq, hkv, d, int(bool(causal)),
+                                    _scale(scale, d), _stream(dev)))
+    return out, lse

@@ -1,0 +1,331 @@
+// libsattn: C ABI host layer. Validates every argument before any launch,
+// picks the kernel instance for (dtype, D, causal, mode), and enqueues it on
+// the caller's stream. Allocates nothing; keeps no mutable global state
+// except a thread-local error message.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/sattn.h"
+#include "fwd_kernel.hpp"
+
+namespace {
+
+using namespace sattn;
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SATTN_OK;
+}
+
+// Positions inside one sequence or slice are kept in 32-bit registers.
+constexpr int64_t kMaxLen = int64_t(1) << 30;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool product(std::initializer_list<int64_t> xs, int64_t* out) {
+  int64_t acc = 1;
+  for (int64_t x : xs)
+    if (!mul_ok(acc, x, &acc)) return false;
+  *out = acc;
+  return true;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.hi <= a.lo || b.hi <= b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+Range range_of(const void* p, int64_t bytes, const char* name) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes), name};
+}
+
+// Outputs must not overlap inputs or each other.
+int check_alias(const Range* ins, int nin, const Range* outs, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j]))
+        return fail(SATTN_ERR_ALIAS, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(SATTN_ERR_ALIAS, "output %s overlaps output %s", outs[i].name, outs[j].name);
+  }
+  return SATTN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(int dtype, int64_t D, float scale) {
+  if (dtype != SATTN_F16 && dtype != SATTN_BF16) return fail(SATTN_ERR_DTYPE, "dtype %d is not F16/BF16", dtype);
+  if (D < 0) return fail(SATTN_ERR_SHAPE, "negative D");
+  if (D != 32 && D != 64 && D != 128) return fail(SATTN_ERR_UNSUPPORTED, "head dim D=%lld not in {32,64,128}", (long long)D);
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(SATTN_ERR_VALUE, "scale must be finite and > 0");
+  return SATTN_OK;
+}
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------- tiles
+// Query rows per workgroup (32 per wave) and keys per tile.
+template <int D, int MODE>
+struct Tile {
+  static constexpr int NW = (MODE == MODE_SPLIT) ? 1 : (D == 128 ? 4 : 2);
+  static constexpr int BM = NW * 32;
+  static constexpr int BN = 64;
+};
+
+template <class E, int D, bool CAUSAL, int MODE>
+void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t s) {
+  using T = Tile<D, MODE>;
+  hipLaunchKernelGGL((fwd_kernel<E, D, T::BN, T::NW, CAUSAL, MODE>), dim3((unsigned)grid), dim3(T::NW * 64), 0, s, p);
+}
+
+template <int MODE>
+int tile_m(int64_t D) {
+  switch (D) {
+    case 32: return Tile<32, MODE>::BM;
+    case 64: return Tile<64, MODE>::BM;
+    default: return Tile<128, MODE>::BM;
+  }
+}
+
+template <int MODE>
+void dispatch_fwd(int dtype, int64_t D, bool causal, const FwdParams& p, int64_t grid, hipStream_t s) {
+#define SATTN_CASE(E_, D_)                                   \
+  if (causal) launch_fwd<E_, D_, true, MODE>(p, grid, s);    \
+  else launch_fwd<E_, D_, false, MODE>(p, grid, s);
+  if (dtype == SATTN_BF16) {
+    if (D == 32) { SATTN_CASE(Bf16, 32) } else if (D == 64) { SATTN_CASE(Bf16, 64) } else { SATTN_CASE(Bf16, 128) }
+  } else {
+    if (D == 32) { SATTN_CASE(F16, 32) } else if (D == 64) { SATTN_CASE(F16, 64) } else { SATTN_CASE(F16, 128) }
+  }
+#undef SATTN_CASE
+}
+
+// The split path is non-causal only.
+void dispatch_split(int dtype, int64_t D, const FwdParams& p, int64_t grid, hipStream_t s) {
+  if (dtype == SATTN_BF16) {
+    if (D == 32) launch_fwd<Bf16, 32, false, MODE_SPLIT>(p, grid, s);
+    else if (D == 64) launch_fwd<Bf16, 64, false, MODE_SPLIT>(p, grid, s);
+    else launch_fwd<Bf16, 128, false, MODE_SPLIT>(p, grid, s);
+  } else {
+    if (D == 32) launch_fwd<F16, 32, false, MODE_SPLIT>(p, grid, s);
+    else if (D == 64) launch_fwd<F16, 64, false, MODE_SPLIT>(p, grid, s);
+    else launch_fwd<F16, 128, false, MODE_SPLIT>(p, grid, s);
+  }
+}
+
+FwdParams blank_params(float scale) {
+  FwdParams p{};
+  p.c = scale * kLog2e;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sattn_status_string(int status) {
+  switch (status) {
+    case SATTN_OK: return "SATTN_OK";
+    case SATTN_ERR_NULL: return "SATTN_ERR_NULL";
+    case SATTN_ERR_SHAPE: return "SATTN_ERR_SHAPE";
+    case SATTN_ERR_DTYPE: return "SATTN_ERR_DTYPE";
+    case SATTN_ERR_UNSUPPORTED: return "SATTN_ERR_UNSUPPORTED";
+    case SATTN_ERR_ALIGN: return "SATTN_ERR_ALIGN";
+    case SATTN_ERR_ALIAS: return "SATTN_ERR_ALIAS";
+    case SATTN_ERR_HIP: return "SATTN_ERR_HIP";
+    case SATTN_ERR_VALUE: return "SATTN_ERR_VALUE";
+    default: return "SATTN_ERR_UNKNOWN";
+  }
+}
+
+const char* sattn_last_error(void) { return g_err; }
+
+int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+              int64_t N, int64_t D, int causal, float scale, void* stream) {
+  int st = check_common(dtype, D, scale);
+  if (st) return st;
+  if (B < 0 || H < 0 || N < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  int64_t heads, rows, elems;
+  if (!product({B, H}, &heads) || !product({heads, N}, &rows) || !product({rows, D, 2}, &elems))
+    return fail(SATTN_ERR_SHAPE, "size overflow");
+  if (N >= kMaxLen || heads >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "N or B*H too large");
+  if (rows == 0) return ok();
+  if (!q || !k || !v || !o || !lse) return fail(SATTN_ERR_NULL, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return fail(SATTN_ERR_ALIGN, "q/k/v/o need 16-byte and lse 4-byte alignment");
+  const int64_t bytes = elems;  // rows * D * 2
+  Range ins[3] = {range_of(q, bytes, "q"), range_of(k, bytes, "k"), range_of(v, bytes, "v")};
+  Range outs[2] = {range_of(o, bytes, "o"), range_of(lse, rows * 4, "lse")};
+  if ((st = check_alias(ins, 3, outs, 2))) return st;
+
+  const int bm = tile_m<MODE_DENSE>(D);
+  const int64_t nqt = (N + bm - 1) / bm;
+  const int64_t grid = nqt * heads;
+  if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
+  FwdParams p = blank_params(scale);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.heads = (int)heads;
+  p.n = (int)N;
+  p.nqt = (int)nqt;
+  dispatch_fwd<MODE_DENSE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+  return launch_status();
+}
+
+int sattn_fwd_split(int dtype, const void* q, const void* k, const void* v, float* part_m, float* part_l,
+                    float* part_acc, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                    int64_t chunk, float scale, void* stream) {
+  int st = check_common(dtype, D, scale);
+  if (st) return st;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  if (chunk <= 0) return fail(SATTN_ERR_SHAPE, "chunk must be > 0");
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return fail(SATTN_ERR_SHAPE, "Hq must be a multiple of Hkv");
+  int64_t qrows, kvrows, qbytes, kvbytes;
+  if (!product({B, Hq, Nq}, &qrows) || !product({B, Hkv, Nk}, &kvrows) || !product({qrows, D, 2}, &qbytes) ||
+      !product({kvrows, D, 2}, &kvbytes))
+    return fail(SATTN_ERR_SHAPE, "size overflow");
+  if (qrows == 0) return ok();
+  if (Nk == 0) return fail(SATTN_ERR_SHAPE, "Nk must be > 0 (a row with no keys has no partials)");
+  if (Nq >= kMaxLen || Nk >= kMaxLen || B * Hq >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "size too large");
+  const int64_t C = (Nk + chunk - 1) / chunk;
+  int64_t prow, mbytes, abytes;
+  if (!product({qrows, C}, &prow) || !product({prow, 4}, &mbytes) || !product({prow, D, 4}, &abytes))
+    return fail(SATTN_ERR_SHAPE, "size overflow");
+  if (!q || !k || !v || !part_m || !part_l || !part_acc) return fail(SATTN_ERR_NULL, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(part_acc, 16) || !aligned(part_m, 4) ||
+      !aligned(part_l, 4))
+    return fail(SATTN_ERR_ALIGN, "q/k/v/part_acc need 16-byte, part_m/part_l 4-byte alignment");
+  Range ins[3] = {range_of(q, qbytes, "q"), range_of(k, kvbytes, "k"), range_of(v, kvbytes, "v")};
+  Range outs[3] = {range_of(part_m, mbytes, "part_m"), range_of(part_l, mbytes, "part_l"),
+                   range_of(part_acc, abytes, "part_acc")};
+  if ((st = check_alias(ins, 3, outs, 3))) return st;
+
+  const int bm = tile_m<MODE_SPLIT>(D);
+  const int64_t nqt = (Nq + bm - 1) / bm;
+  const int64_t grid = qrows / Nq * nqt * C;
+  if (grid >= (int64_t(1) << 31) || C >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
+  FwdParams p = blank_params(scale);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.part_m = part_m;
+  p.part_l = part_l;
+  p.part_acc = part_acc;
+  p.heads = (int)(B * Hq);
+  p.hq = (int)Hq;
+  p.hkv = (int)Hkv;
+  p.n = (int)Nq;
+  p.nk = (int)Nk;
+  p.chunk = (int)(chunk < Nk ? chunk : Nk);  // chunk >= Nk: one chunk holds every key
+  p.nchunks = (int)C;
+  p.nqt = (int)nqt;
+  dispatch_split(dtype, D, p, grid, (hipStream_t)stream);
+  return launch_status();
+}
+
+int sattn_merge(int dtype, const float* part_m, const float* part_l, const float* part_acc, int64_t rows, int64_t C,
+                int64_t D, void* o, float* lse, void* stream) {
+  int st = check_common(dtype, D, 1.0f);
+  if (st) return st;
+  if (rows < 0 || C < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  if (rows == 0) return ok();
+  if (C == 0) return fail(SATTN_ERR_SHAPE, "C must be > 0");
+  int64_t prow, mbytes, abytes, obytes;
+  if (!product({rows, C}, &prow) || !product({prow, 4}, &mbytes) || !product({prow, D, 4}, &abytes) ||
+      !product({rows, D, 2}, &obytes))
+    return fail(SATTN_ERR_SHAPE, "size overflow");
+  if (C >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "C too large");
+  if (!part_m || !part_l || !part_acc || !o || !lse) return fail(SATTN_ERR_NULL, "null pointer");
+  if (!aligned(part_m, 4) || !aligned(part_l, 4) || !aligned(part_acc, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return fail(SATTN_ERR_ALIGN, "misaligned pointer");
+  Range ins[3] = {range_of(part_m, mbytes, "part_m"), range_of(part_l, mbytes, "part_l"),
+                  range_of(part_acc, abytes, "part_acc")};
+  Range outs[2] = {range_of(o, obytes, "o"), range_of(lse, rows * 4, "lse")};
+  if ((st = check_alias(ins, 3, outs, 2))) return st;
+  const int64_t grid = (rows + 3) / 4;
+  if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
+  hipStream_t s = (hipStream_t)stream;
+  const int c = (int)C;
+  uint16_t* out = (uint16_t*)o;
+#define SATTN_MERGE(E_, D_) \
+  hipLaunchKernelGGL((merge_kernel<E_, D_>), dim3((unsigned)grid), dim3(256), 0, s, part_m, part_l, part_acc, rows, c, out, lse)
+  if (dtype == SATTN_BF16) {
+    if (D == 32) SATTN_MERGE(Bf16, 32); else if (D == 64) SATTN_MERGE(Bf16, 64); else SATTN_MERGE(Bf16, 128);
+  } else {
+    if (D == 32) SATTN_MERGE(F16, 32); else if (D == 64) SATTN_MERGE(F16, 64); else SATTN_MERGE(F16, 128);
+  }
+#undef SATTN_MERGE
+  return launch_status();
+}
+
+int sattn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* cu_seqlens, int64_t S, int64_t T, int64_t max_seqlen, int64_t Hq, int64_t Hkv,
+                     int64_t D, int causal, float scale, void* stream) {
+  int st = check_common(dtype, D, scale);
+  if (st) return st;
+  if (S < 0 || T < 0 || max_seqlen < 0 || Hq < 0 || Hkv < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return fail(SATTN_ERR_SHAPE, "Hq must be a multiple of Hkv");
+  int64_t qbytes, kvbytes, lbytes;
+  if (!product({T, Hq, D, 2}, &qbytes) || !product({T, Hkv, D, 2}, &kvbytes) || !product({Hq, T, 4}, &lbytes))
+    return fail(SATTN_ERR_SHAPE, "size overflow");
+  if (S == 0 || T == 0 || Hq == 0 || max_seqlen == 0) return ok();
+  if (T >= kMaxLen || S >= kMaxLen || Hq >= 65536 || max_seqlen > T)
+    return fail(max_seqlen > T ? SATTN_ERR_SHAPE : SATTN_ERR_UNSUPPORTED, "max_seqlen > T or size too large");
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return fail(SATTN_ERR_NULL, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(cu_seqlens, 4))
+    return fail(SATTN_ERR_ALIGN, "misaligned pointer");
+  Range ins[4] = {range_of(q, qbytes, "q"), range_of(k, kvbytes, "k"), range_of(v, kvbytes, "v"),
+                  range_of(cu_seqlens, (S + 1) * 4, "cu_seqlens")};
+  Range outs[2] = {range_of(o, qbytes, "o"), range_of(lse, lbytes, "lse")};
+  if ((st = check_alias(ins, 4, outs, 2))) return st;
+  const int bm = tile_m<MODE_VARLEN>(D);
+  const int64_t nqt = (max_seqlen + bm - 1) / bm;
+  int64_t grid;
+  if (!product({nqt, S, Hq}, &grid) || grid >= (int64_t(1) << 31))
+    return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
+  FwdParams p = blank_params(scale);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.hq = (int)Hq;
+  p.hkv = (int)Hkv;
+  p.nqt = (int)nqt;
+  p.nseq = (int)S;
+  p.total = (int)T;
+  dispatch_fwd<MODE_VARLEN>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+  return launch_status();
+}
+
+}  // extern "C"

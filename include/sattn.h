@@ -1,0 +1,154 @@
+/*
+ * sattn.h -- exact streaming (tiled) attention forward for AMD gfx950.
+ *
+ * C ABI of libsattn.so. Every entry point takes plain device pointers and
+ * sizes; no framework types cross this boundary.
+ *
+ * What is computed (one query row i, eligible keys j):
+ *   S_ij = scale * <q_i, k_j>,  m_i = max_j S_ij,  l_i = sum_j exp(S_ij - m_i)
+ *   O_i  = sum_j exp(S_ij - m_i) v_j / l_i,        lse_i = m_i + ln(l_i)
+ * computed tile by tile over K/V with a mergeable (running max, rescaled
+ * exp-sum, rescaled numerator) state, never forming the full score matrix.
+ * Sources: "Intermediate and advanced extension" (workshop table, streaming
+ * attention and split softmax rows; "Logic review before implementation":
+ * numerator and denominator are both rescaled, causal rows include their
+ * diagonal, a kernel boundary on one stream orders dependent launches);
+ * "Attention algorithms and data movement", lessons 01 (merge partial states
+ * by rescaled denominators, explicit empty-row contract), 03 (saved per-row
+ * normalization state = lse), 04 (packed causal eligibility by logical
+ * position), 05 (GQA query-head to KV-head mapping).
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * - dtype: SATTN_F16 (IEEE binary16) or SATTN_BF16 (bfloat16) for q, k, v, o.
+ *   Products use fp16/bf16 inputs with fp32 accumulation; the softmax state
+ *   is fp32; P is rounded to the input dtype for the P*V product while the
+ *   exp-sum l accumulates the fp32 values; O is rounded once (nearest-even).
+ * - lse is float32, natural log, of the scaled scores.
+ * - Head dimension D must be 32, 64 or 128.
+ * - scale must be finite and > 0 (the caller passes e.g. 1/sqrt(D)).
+ * - Pointers are device pointers on the current HIP device. q, k, v, o must
+ *   be 16-byte aligned, float buffers 4-byte aligned. Inputs are read-only;
+ *   outputs must not overlap any input or each other (byte ranges).
+ * - stream: a hipStream_t (NULL = the default stream). All work is enqueued
+ *   on it asynchronously; nothing synchronizes the host.
+ * - Ownership: the caller allocates and owns every buffer, including the
+ *   split-KV partial buffers. The library allocates no device memory and
+ *   keeps no mutable global state; calls are thread-safe.
+ * - Errors: every argument check happens before any launch. On error nothing
+ *   is enqueued and outputs are untouched; the return value says why and
+ *   sattn_last_error() gives a message (thread-local). A zero-size problem
+ *   (for example B, H or N equal to 0) returns SATTN_OK and enqueues nothing;
+ *   its pointers may then be NULL.
+ * - Every output element is written; outputs need no initialization.
+ */
+#ifndef SATTN_H
+#define SATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SATTN_F16 = 0,
+  SATTN_BF16 = 1
+} sattn_dtype_t;
+
+typedef enum {
+  SATTN_OK = 0,
+  SATTN_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  SATTN_ERR_SHAPE = 2,       /* negative, inconsistent or overflowing sizes    */
+  SATTN_ERR_DTYPE = 3,       /* dtype is not SATTN_F16 / SATTN_BF16            */
+  SATTN_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. D = 96)        */
+  SATTN_ERR_ALIGN = 5,       /* pointer misaligned                             */
+  SATTN_ERR_ALIAS = 6,       /* an output overlaps an input or another output  */
+  SATTN_ERR_HIP = 7,         /* the HIP runtime reported an error at launch    */
+  SATTN_ERR_VALUE = 8        /* bad scalar argument (scale not finite or <= 0) */
+} sattn_status_t;
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* sattn_status_string(int status);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* sattn_last_error(void);
+
+/*
+ * Batched multi-head attention forward ("Intermediate and advanced
+ * extension", workshop table, streaming-attention row: tile QK and PV with
+ * online rescaling, causal and noncausal self-attention).
+ *
+ *   q, k, v, o : [B, H, N, D] contiguous, D innermost, dtype `dtype`.
+ *   lse        : [B, H, N] float32.
+ *   causal     : nonzero -> key j is eligible for query i iff j <= i
+ *                (diagonal included; equal query and key lengths).
+ * Key tiles wholly above the diagonal are skipped, not masked.
+ */
+int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+              int64_t B, int64_t H, int64_t N, int64_t D, int causal, float scale,
+              void* stream);
+
+/*
+ * Split-KV partial states, non-causal ("Intermediate and advanced
+ * extension", workshop table, split-softmax row: partial statistics as a
+ * launch of their own; here applied to attention with K/V split into chunks).
+ *
+ *   q          : [B, Hq, Nq, D];  k, v : [B, Hkv, Nk, D]  (dtype `dtype`).
+ *   Query head h reads KV head h / (Hq / Hkv); Hq % Hkv must be 0.
+ *   chunk      : keys per chunk (> 0); C = ceil(Nk / chunk) chunks, chunk c
+ *                covering keys [c*chunk, min(Nk, (c+1)*chunk)).
+ *   part_m     : [B, Hq, Nq, C] float32, max scaled score of the chunk.
+ *   part_l     : [B, Hq, Nq, C] float32, sum over the chunk of exp(S - m).
+ *   part_acc   : [B, Hq, Nq, C, D] float32, sum of exp(S - m) * v,
+ *                NOT divided by l.
+ * The three buffers are private to this call and its following
+ * sattn_merge (enqueue the merge on the same stream, or after an event).
+ * Nk must be > 0 when B*Hq*Nq > 0. Causal split is not implemented
+ * (there is no causal argument).
+ */
+int sattn_fwd_split(int dtype, const void* q, const void* k, const void* v,
+                    float* part_m, float* part_l, float* part_acc,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                    int64_t chunk, float scale, void* stream);
+
+/*
+ * Merge of partial states ("Attention algorithms and data movement",
+ * lesson 01: combine by rescaled denominators, never average).
+ *
+ *   part_m, part_l : [rows, C] float32;  part_acc : [rows, C, D] float32.
+ *   o              : [rows, D] dtype `dtype`;  lse : [rows] float32.
+ * With M = max_c m_c and w_c = exp(m_c - M): L = sum_c w_c l_c,
+ * O = sum_c w_c acc_c / L, lse = M + ln L, summed in ascending c.
+ * An empty partial (m = -inf, l = 0) is the identity; a row whose partials
+ * are all empty gives O = 0 and lse = -inf.
+ */
+int sattn_merge(int dtype, const float* part_m, const float* part_l, const float* part_acc,
+                int64_t rows, int64_t C, int64_t D, void* o, float* lse, void* stream);
+
+/*
+ * Packed variable-length grouped-query attention ("Attention algorithms and
+ * data movement", lessons 04 and 05).
+ *
+ *   q, o       : [T, Hq, D];  k, v : [T, Hkv, D]  (dtype `dtype`).
+ *   lse        : [Hq, T] float32.
+ *   cu_seqlens : device int32 [S + 1]; sequence s owns tokens
+ *                [cu[s], cu[s+1]). The caller guarantees cu[0] = 0,
+ *                non-decreasing, cu[S] = T and every length <= max_seqlen
+ *                (checked by the Python binding on its host copy; the kernel
+ *                clamps every index into [0, T) so a bad table cannot read
+ *                or write out of bounds).
+ *   Query head h reads KV head h / (Hq / Hkv); Hq % Hkv must be 0.
+ *   Tokens attend only to keys of their own sequence; causal eligibility uses
+ *   positions within the sequence (key r' is eligible for query r iff
+ *   r' <= r, diagonal included).
+ */
+int sattn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int32_t* cu_seqlens, int64_t S, int64_t T, int64_t max_seqlen,
+                     int64_t Hq, int64_t Hkv, int64_t D, int causal, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SATTN_H */

@@ -1,0 +1,156 @@
+"""The C ABI library loads, exports every symbol the header declares, and
+rejects invalid calls before any launch (CPU only: no call here reaches the
+HIP runtime; each case fails one of the host-side checks).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_sattn_amd import LIB_PATH, STATUS, library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sattn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sattn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from exact_tiled_attention_sattn_amd import build
+        build.build()
+    return library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen",
+              "sattn_status_string", "sattn_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), "libsattn.so does not export %s" % name
+
+
+def test_status_strings(lib):
+    for code, name in STATUS.items():
+        assert lib.sattn_status_string(code).decode() == name
+    assert lib.sattn_status_string(99).decode() == "SATTN_ERR_UNKNOWN"
+
+
+I64 = ctypes.c_int64
+F32 = ctypes.c_float
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: every call below fails validation first
+FAKE2 = ctypes.c_void_p(0x20000)
+FAKE3 = ctypes.c_void_p(0x30000)
+FAKE4 = ctypes.c_void_p(0x40000)
+FAKE5 = ctypes.c_void_p(0x50000)
+NULL = ctypes.c_void_p(0)
+
+
+def _fwd(lib, dtype=1, q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5, b=1, h=1, n=8, d=64, causal=0, scale=0.125):
+    return lib.sattn_fwd(dtype, q, k, v, o, lse, b, h, n, d, causal, scale, NULL)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=7), "SATTN_ERR_DTYPE"),
+    (dict(d=96), "SATTN_ERR_UNSUPPORTED"),
+    (dict(d=-1), "SATTN_ERR_SHAPE"),
+    (dict(n=-3), "SATTN_ERR_SHAPE"),
+    (dict(scale=0.0), "SATTN_ERR_VALUE"),
+    (dict(scale=-1.0), "SATTN_ERR_VALUE"),
+    (dict(scale=float("nan")), "SATTN_ERR_VALUE"),
+    (dict(scale=float("inf")), "SATTN_ERR_VALUE"),
+    (dict(q=NULL), "SATTN_ERR_NULL"),
+    (dict(lse=NULL), "SATTN_ERR_NULL"),
+    (dict(q=ctypes.c_void_p(0x10008)), "SATTN_ERR_ALIGN"),
+    (dict(lse=ctypes.c_void_p(0x50002)), "SATTN_ERR_ALIGN"),
+    (dict(o=FAKE), "SATTN_ERR_ALIAS"),                          # o == q
+    (dict(o=ctypes.c_void_p(0x10000 + 512)), "SATTN_ERR_ALIAS"),  # o inside q's 1 KiB
+    (dict(lse=ctypes.c_void_p(0x40000 + 16)), "SATTN_ERR_ALIAS"),  # lse inside o
+    (dict(b=1 << 40, h=1 << 40), "SATTN_ERR_SHAPE"),              # element count overflows
+    (dict(n=1 << 31), "SATTN_ERR_UNSUPPORTED"),
+])
+def test_fwd_rejects(lib, kwargs, status):
+    st = _fwd(lib, **kwargs)
+    assert STATUS[st] == status, (STATUS[st], lib.sattn_last_error())
+    assert lib.sattn_last_error().decode() != ""
+
+
+def test_fwd_zero_size_is_ok_without_pointers(lib):
+    assert _fwd(lib, q=NULL, k=NULL, v=NULL, o=NULL, lse=NULL, n=0) == 0
+    assert _fwd(lib, q=NULL, k=NULL, v=NULL, o=NULL, lse=NULL, b=0) == 0
+
+
+def _split(lib, b=1, hq=4, hkv=2, nq=1, nk=100, d=128, chunk=32, q=FAKE, k=FAKE2, v=FAKE3,
+           pm=ctypes.c_void_p(0x900000), pl=ctypes.c_void_p(0xA00000), pa=ctypes.c_void_p(0xB00000)):
+    return lib.sattn_fwd_split(1, q, k, v, pm, pl, pa, b, hq, hkv, nq, nk, d, chunk, F32(0.1), NULL)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(chunk=0), "SATTN_ERR_SHAPE"),
+    (dict(chunk=-5), "SATTN_ERR_SHAPE"),
+    (dict(hq=6, hkv=4), "SATTN_ERR_SHAPE"),
+    (dict(hkv=0), "SATTN_ERR_SHAPE"),
+    (dict(nk=0), "SATTN_ERR_SHAPE"),
+    (dict(d=48), "SATTN_ERR_UNSUPPORTED"),
+    (dict(pa=NULL), "SATTN_ERR_NULL"),
+    (dict(pa=ctypes.c_void_p(0xB00004)), "SATTN_ERR_ALIGN"),
+    (dict(pm=FAKE2), "SATTN_ERR_ALIAS"),
+    (dict(pl=ctypes.c_void_p(0x900000)), "SATTN_ERR_ALIAS"),
+])
+def test_split_rejects(lib, kwargs, status):
+    st = _split(lib, **kwargs)
+    assert STATUS[st] == status, (STATUS[st], lib.sattn_last_error())
+
+
+def test_split_zero_rows_ok(lib):
+    assert _split(lib, nq=0, q=NULL, k=NULL, v=NULL, pm=NULL, pl=NULL, pa=NULL) == 0
+
+
+def test_merge_rejects(lib):
+    pm, pl, pa = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    o, lse = ctypes.c_void_p(0x400000), ctypes.c_void_p(0x500000)
+    assert STATUS[lib.sattn_merge(1, pm, pl, pa, 4, 0, 128, o, lse, NULL)] == "SATTN_ERR_SHAPE"
+    assert STATUS[lib.sattn_merge(1, pm, pl, pa, -1, 2, 128, o, lse, NULL)] == "SATTN_ERR_SHAPE"
+    assert STATUS[lib.sattn_merge(2, pm, pl, pa, 4, 2, 128, o, lse, NULL)] == "SATTN_ERR_DTYPE"
+    assert STATUS[lib.sattn_merge(1, pm, pl, pa, 4, 2, 128, pa, lse, NULL)] == "SATTN_ERR_ALIAS"
+    assert STATUS[lib.sattn_merge(1, pm, pl, NULL, 4, 2, 128, o, lse, NULL)] == "SATTN_ERR_NULL"
+    assert lib.sattn_merge(1, NULL, NULL, NULL, 0, 2, 128, NULL, NULL, NULL) == 0
+
+
+def test_varlen_rejects(lib):
+    cu = ctypes.c_void_p(0x600000)
+
+    def call(**kw):
+        a = dict(dtype=1, q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5, cu=cu, s=2, t=10, mx=6, hq=4,
+                 hkv=2, d=64, causal=1, scale=0.1)
+        a.update(kw)
+        return STATUS[lib.sattn_fwd_varlen(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["s"],
+                                           a["t"], a["mx"], a["hq"], a["hkv"], a["d"], a["causal"],
+                                           F32(a["scale"]), NULL)]
+    assert call(hq=3) == "SATTN_ERR_SHAPE"
+    assert call(mx=11) == "SATTN_ERR_SHAPE"
+    assert call(cu=NULL) == "SATTN_ERR_NULL"
+    assert call(cu=ctypes.c_void_p(0x600002)) == "SATTN_ERR_ALIGN"
+    assert call(o=FAKE) == "SATTN_ERR_ALIAS"
+    assert call(lse=cu) == "SATTN_ERR_ALIAS"
+    assert call(d=16) == "SATTN_ERR_UNSUPPORTED"
+    assert call(t=0, q=NULL, k=NULL, v=NULL, o=NULL, lse=NULL, cu=NULL) == "SATTN_OK"
+
+
+def test_binding_checks_cu_seqlens_on_host():
+    from exact_tiled_attention_sattn_amd import check_cu_seqlens
+    check_cu_seqlens([0, 3, 3, 10], 10, 7)
+    for bad, t, mx in (([1, 3], 3, 5), ([0, 5, 4], 4, 5), ([0, 4], 5, 5), ([0, 9], 9, 8)):
+        with pytest.raises(ValueError):
+            check_cu_seqlens(bad, t, mx)

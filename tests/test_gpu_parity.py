@@ -1,0 +1,355 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 oracle.
+
+Inputs come from the seeded generators in ``workloads``; expected values come
+only from ``oracle``. Small cases are compared in full (several tiles and a
+ragged tail); the full-size workloads are compared on seeded samples of rows
+the oracle computes one by one.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from exact_tiled_attention_sattn_amd import (sattn_fwd, sattn_fwd_split, sattn_merge, sattn_fwd_varlen,
+                                             SattnError)
+from oracle import dense
+from tests.parity import check_attention, check_o, check_lse, TOL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _banner(*a):
+    print("[case]", *a, flush=True)
+
+
+def _dense_inputs(b, h, n, d, dtype, seed, qmul=1.0):
+    q, k, v = W.qkv((b, h, n, d), (b, h, n, d), dtype, seed)
+    if qmul != 1.0:
+        q = (q.float() * qmul).to(q.dtype)   # power of two: exact
+    return q, k, v
+
+
+def _run_fwd(q, k, v, causal, scale):
+    o, lse = sattn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------ dense, small
+SMALL = [
+    # (B, H, N, D, dtype)
+    (1, 1, 1, 32, "fp16"), (1, 1, 2, 64, "bf16"), (1, 2, 31, 128, "bf16"), (2, 3, 65, 32, "fp16"),
+    (1, 2, 127, 64, "bf16"), (1, 1, 129, 128, "fp16"), (2, 2, 200, 64, "fp16"), (1, 3, 333, 128, "bf16"),
+    (1, 1, 257, 32, "bf16"), (1, 2, 513, 128, "fp16"),
+]
+
+
+@pytest.mark.parametrize("b,h,n,d,dt", SMALL)
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_small_full(b, h, n, d, dt, causal):
+    _banner("dense", b, h, n, d, dt, causal)
+    q, k, v = _dense_inputs(b, h, n, d, dt, seed=1000 + n + d + h)
+    scale = W.scale_f32(d)
+    o, lse = _run_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "dense")
+
+
+def test_c1_single_head_129x32_fp16_causal():
+    cfg = W.WORKLOADS["single_head_129x32_fp16_causal"]
+    _banner("129x32 fp16 causal")
+    q, k, v = _dense_inputs(1, 1, 129, 32, "fp16", cfg["seed"])
+    scale = W.scale_f32(32)
+    o, lse = _run_fwd(q, k, v, True, scale)
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, True)
+    check_attention(o, lse, o_ref, lse_ref, torch.float16, "129x32")
+
+
+@pytest.mark.parametrize("qmul", [1.0, 16.0])
+@pytest.mark.parametrize("causal", [True, False])
+def test_c2_single_head_512x64_fp16(causal, qmul):
+    cfg = W.WORKLOADS["single_head_512x64_fp16"]
+    _banner("512x64 fp16", causal, qmul)
+    q, k, v = _dense_inputs(1, 1, 512, 64, "fp16", cfg["seed"], qmul)
+    scale = W.scale_f32(64)
+    o, lse = _run_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, torch.float16, "512x64")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_c3_batched_4x16x4096x128_bf16_sampled(causal):
+    cfg = W.WORKLOADS["batched_4x16x4096x128_bf16"]
+    _banner("4x16x4096x128 bf16", causal)
+    b, h, n, d = 4, 16, 4096, 128
+    q, k, v = _dense_inputs(b, h, n, d, "bf16", cfg["seed"])
+    scale = W.scale_f32(d)
+    o, lse = _run_fwd(q, k, v, causal, scale)
+    rows = W.sample_rows(cfg["seed"], n, cfg["sampled_rows_per_head"], groups=b * h).reshape(b, h, -1)
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal, rows=rows)
+    idx = torch.from_numpy(rows)
+    o_s = torch.stack([torch.stack([o[i, j].cpu()[idx[i, j]] for j in range(h)]) for i in range(b)])
+    lse_s = torch.stack([torch.stack([lse[i, j].cpu()[idx[i, j]] for j in range(h)]) for i in range(b)])
+    check_attention(o_s, lse_s, o_ref, lse_ref, torch.bfloat16, "4096x128")
+    # every row written and finite (outputs were fresh torch.empty)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+# ------------------------------------------------------- closed form on GPU
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_zero_q_gives_mean_of_values(dt):
+    """Q = 0: every eligible score is 0, P = 1 exactly; O_i = mean(V[0..i])
+    causal, lse_i = ln(i+1)."""
+    _banner("zero-q", dt)
+    n, d = 300, 64
+    _, k, v = _dense_inputs(1, 1, n, d, dt, seed=77)
+    q = torch.zeros_like(k)
+    o, lse = _run_fwd(q, k, v, True, 0.125)
+    vv = W.to_f64(v)[0, 0]
+    ref = np.cumsum(vv, axis=0) / np.arange(1, n + 1)[:, None]
+    check_o(o[0, 0], ref, W.DTYPES[dt], "zero-q o")
+    check_lse(lse[0, 0], np.log(np.arange(1, n + 1)), "zero-q lse")
+
+
+# ------------------------------------------------------------ invariants
+def test_causal_future_perturbation_bitwise():
+    _banner("future perturbation")
+    n, d = 512, 64
+    q, k, v = _dense_inputs(1, 2, n, d, "fp16", seed=2)
+    o0, l0 = _run_fwd(q, k, v, True, 0.125)
+    for j in (1, 64, 65, 300, 511):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, :, j] = 30.0
+        v2[:, :, j] = -500.0
+        o1, l1 = _run_fwd(q, k2, v2, True, 0.125)
+        assert torch.equal(o1[:, :, :j], o0[:, :, :j]), j
+        assert torch.equal(l1[:, :, :j], l0[:, :, :j]), j
+        assert not torch.equal(o1[:, :, j:], o0[:, :, j:])
+
+
+def test_deterministic_bitwise_and_inputs_preserved():
+    _banner("determinism")
+    q, k, v = (x.to(DEV) for x in _dense_inputs(2, 4, 700, 128, "bf16", seed=9))
+    digest = [hashlib.sha256(x.cpu().view(torch.int16).numpy().tobytes()).hexdigest() for x in (q, k, v)]
+    a = sattn_fwd(q, k, v, causal=True)
+    b = sattn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    after = [hashlib.sha256(x.cpu().view(torch.int16).numpy().tobytes()).hexdigest() for x in (q, k, v)]
+    assert after == digest
+
+
+def test_fresh_outputs_overwritten_and_nondefault_stream():
+    _banner("fresh outputs / stream")
+    q, k, v = (x.to(DEV) for x in _dense_inputs(1, 3, 257, 64, "fp16", seed=10))
+    ref = sattn_fwd(q, k, v, causal=False)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sattn_fwd(q, k, v, causal=False, out=out, lse=lse)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+
+
+def test_alias_rejected_on_device():
+    q, k, v = (x.to(DEV) for x in _dense_inputs(1, 1, 64, 64, "fp16", seed=11))
+    with pytest.raises(SattnError, match="ALIAS"):
+        sattn_fwd(q, k, v, out=q)
+
+
+# ---------------------------------------------------------------- split
+SPLIT_SMALL = [
+    # (B, Hq, Hkv, Nq, Nk, D, chunk, dtype)
+    (1, 2, 2, 1, 100, 128, 32, "bf16"),
+    (2, 4, 1, 1, 4096, 128, 1024, "bf16"),
+    (1, 4, 2, 3, 777, 64, 256, "fp16"),
+    (1, 1, 1, 40, 130, 32, 64, "fp16"),
+    (1, 2, 1, 1, 50, 128, 4096, "bf16"),       # one chunk larger than Nk
+    (1, 1, 1, 2, 65, 64, 1, "bf16"),           # one key per chunk
+]
+
+
+@pytest.mark.parametrize("b,hq,hkv,nq,nk,d,chunk,dt", SPLIT_SMALL)
+def test_split_partials_and_merge_small(b, hq, hkv, nq, nk, d, chunk, dt):
+    _banner("split", b, hq, hkv, nq, nk, d, chunk, dt)
+    q, k, v = W.qkv((b, hq, nq, d), (b, hkv, nk, d), dt, seed=2000 + nk)
+    scale = W.scale_f32(d)
+    pm, pl, pa = sattn_fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), chunk, scale)
+    o, lse = sattn_merge(pm, pl, pa, W.DTYPES[dt])
+    torch.cuda.synchronize()
+    qf, kf, vf = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    g = hq // hkv
+    pm_, pl_, pa_ = (x.cpu().double().numpy() for x in (pm, pl, pa))
+    for bb in range(b):
+        for h in range(hq):
+            m_ref, l_ref, a_ref = dense.split_partials(qf[bb, h], kf[bb, h // g], vf[bb, h // g], scale, chunk)
+            # each partial: its max, its logsumexp and its normalized output
+            np.testing.assert_allclose(pm_[bb, h], m_ref, rtol=0, atol=1e-3)
+            check_lse(pm_[bb, h] + np.log(pl_[bb, h]), m_ref + np.log(l_ref), "partial lse")
+            check_o(pa_[bb, h] / pl_[bb, h][..., None], a_ref / l_ref[..., None], W.DTYPES[dt], "partial o")
+            o_ref, lse_ref = dense.attention(qf[bb, h], kf[bb, h // g], vf[bb, h // g], scale)
+            check_attention(o[bb, h], lse[bb, h], o_ref, lse_ref, W.DTYPES[dt], "merged")
+
+
+def test_split_matches_fwd():
+    _banner("split vs fwd")
+    q, k, v = (x.to(DEV) for x in _dense_inputs(1, 4, 1000, 128, "bf16", seed=12))
+    o1, l1 = sattn_fwd(q, k, v, causal=False)
+    pm, pl, pa = sattn_fwd_split(q, k, v, 256)
+    o2, l2 = sattn_merge(pm, pl, pa, torch.bfloat16)
+    torch.cuda.synchronize()
+    tol = TOL[torch.bfloat16]
+    assert (o1.float() - o2.float()).abs().max().item() <= tol[0] + tol[1]
+    assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+def test_merge_empty_partials_identity():
+    """Empty partials (m=-inf, l=0, acc=0) change nothing; all-empty rows give
+    O = 0, lse = -inf."""
+    _banner("merge empty")
+    rows, c, d = 5, 6, 128
+    g = torch.Generator().manual_seed(13)
+    pm = torch.randn(rows, c, generator=g) * 3
+    pl = torch.rand(rows, c, generator=g) * 10 + 1
+    pa = torch.randn(rows, c, d, generator=g) * 5
+    pm[1, 2] = -float("inf"); pl[1, 2] = 0; pa[1, 2] = 0
+    pm[3, :] = -float("inf"); pl[3, :] = 0; pa[3, :] = 0
+    o, lse = sattn_merge(pm.to(DEV), pl.to(DEV), pa.to(DEV), torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.merge_partials(pm.double().numpy(), pl.double().numpy(), pa.double().numpy())
+    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "merge")
+    assert torch.equal(o[3].float().cpu(), torch.zeros(d)) and lse[3].item() == -float("inf")
+
+
+def test_c4_splitkv_decode_full_size_sampled():
+    """16x32 query rows, 131072 keys each, 4096-key chunks; every row's merged
+    output is checked for finiteness; 24 seeded rows against the oracle."""
+    cfg = W.WORKLOADS["splitkv_decode_16x32x131072x128_bf16"]
+    _banner("decode 16x32x131072x128 bf16")
+    b, hq, hkv, nk, d, chunk = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Nk"], cfg["D"], cfg["chunk"]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(cfg["seed"])
+    q = W.randn_device_sliced((b, hq, 1, d), "bf16", g, DEV)
+    k = W.randn_device_sliced((b, hkv, nk, d), "bf16", g, DEV)
+    v = W.randn_device_sliced((b, hkv, nk, d), "bf16", g, DEV)
+    scale = W.scale_f32(d)
+    pm, pl, pa = sattn_fwd_split(q, k, v, chunk, scale)
+    o, lse = sattn_merge(pm, pl, pa, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert pm.shape == (b, hq, 1, 32)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(cfg["seed"])
+    picks = rng.choice(b * hq, size=24, replace=False)
+    for flat in picks:
+        bb, h = divmod(int(flat), hq)
+        qf = W.to_f64(q[bb, h])
+        kf = W.to_f64(k[bb, h])
+        vf = W.to_f64(v[bb, h])
+        o_ref, lse_ref = dense.attention(qf, kf, vf, scale)
+        check_attention(o[bb, h], lse[bb, h], o_ref, lse_ref, torch.bfloat16, "decode row %d" % flat)
+    del k, v
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------- varlen
+def _varlen_inputs(lengths, hq, hkv, d, dt, seed):
+    t = int(sum(lengths))
+    q, k, v = W.qkv((t, hq, d), (t, hkv, d), dt, seed)
+    cu = W.cu_seqlens_of(lengths)
+    return q, k, v, cu
+
+
+VARLEN_SMALL = [
+    # (lengths, Hq, Hkv, D, dtype, causal)
+    ([5, 1, 130, 64], 4, 1, 128, "bf16", True),
+    ([200, 0, 33], 8, 2, 64, "fp16", True),
+    ([1], 2, 2, 32, "fp16", True),
+    ([300, 129, 7], 4, 4, 128, "bf16", False),
+    ([64, 64, 65], 32, 8, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,d,dt,causal", VARLEN_SMALL)
+def test_varlen_small_full(lengths, hq, hkv, d, dt, causal):
+    _banner("varlen", lengths, hq, hkv, d, dt, causal)
+    q, k, v, cu = _varlen_inputs(lengths, hq, hkv, d, dt, seed=3000 + sum(lengths))
+    scale = W.scale_f32(d)
+    o, lse = sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(cu), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.varlen_gqa(W.to_f64(q), W.to_f64(k), W.to_f64(v), cu, scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "varlen")
+
+
+def test_varlen_gqa_equals_expanded_heads_bitwise():
+    _banner("gqa vs expanded")
+    q, k, v, cu = _varlen_inputs([100, 37], 8, 2, 128, "bf16", seed=14)
+    cu_t = torch.from_numpy(cu)
+    o1, l1 = sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_t)
+    ke = k.repeat_interleave(4, dim=1).contiguous()
+    ve = v.repeat_interleave(4, dim=1).contiguous()
+    o2, l2 = sattn_fwd_varlen(q.to(DEV), ke.to(DEV), ve.to(DEV), cu_t)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_varlen_cross_sequence_isolation_bitwise():
+    _banner("cross-sequence")
+    lengths = [150, 90, 200]
+    q, k, v, cu = _varlen_inputs(lengths, 4, 2, 64, "fp16", seed=15)
+    cu_t = torch.from_numpy(cu)
+    o0, l0 = sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_t)
+    a, b = int(cu[1]), int(cu[2])
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[a:b] = 3.0
+    k2[a:b] = -2.0
+    v2[a:b] = 100.0
+    o1, l1 = sattn_fwd_varlen(q2.to(DEV), k2.to(DEV), v2.to(DEV), cu_t)
+    torch.cuda.synchronize()
+    for x, y in ((0, a), (b, int(cu[3]))):
+        assert torch.equal(o1[x:y], o0[x:y]) and torch.equal(l1[:, x:y], l0[:, x:y])
+
+
+def test_varlen_matches_dense_per_sequence_bitwise():
+    """A packed sequence gives the same bits as the batched kernel on it."""
+    _banner("varlen vs dense")
+    q, k, v, cu = _varlen_inputs([257], 4, 4, 128, "bf16", seed=16)
+    o1, l1 = sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(cu))
+    qd, kd, vd = (x.permute(1, 0, 2)[None].contiguous().to(DEV) for x in (q, k, v))
+    o2, l2 = sattn_fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[0].permute(1, 0, 2)) and torch.equal(l1, l2[0])
+
+
+def test_c5_varlen_gqa_full_size_sampled():
+    cfg = W.WORKLOADS["varlen_gqa_8seq_32q8kv_128_bf16_causal"]
+    lengths = W.varlen_lengths(cfg["seed"], cfg["S"], cfg["max_len"])
+    _banner("varlen gqa full", lengths.tolist())
+    hq, hkv, d = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    q, k, v, cu = _varlen_inputs(lengths, hq, hkv, d, "bf16", cfg["seed"])
+    scale = W.scale_f32(d)
+    o, lse = sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(cu), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rows = {}
+    for s, L in enumerate(lengths):
+        for h in range(hq):
+            rows[(s, h)] = W.sample_rows(cfg["seed"] * 1000 + s * 64 + h, int(L), 16)[0]
+    ref = dense.varlen_gqa(W.to_f64(q), W.to_f64(k), W.to_f64(v), cu, scale, True, rows=rows)
+    o_c, l_c = o.cpu(), lse.cpu()
+    for (s, h), r in rows.items():
+        t = int(cu[s]) + torch.from_numpy(r)
+        check_attention(o_c[t, h], l_c[h, t], ref[(s, h)][0], ref[(s, h)][1], torch.bfloat16,
+                        "seq %d head %d" % (s, h))
+
+
+def test_varlen_bad_table_rejected_by_binding():
+    q, k, v, cu = _varlen_inputs([10, 10], 2, 1, 64, "bf16", seed=17)
+    bad = torch.tensor([0, 12, 20], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), bad, max_seqlen=10)

@@ -141,24 +141,64 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
   }
 }
 
+// 16-byte piece swizzle of a K/V tile row in LDS. A row of D bf16/fp16
+// values is PPR = D/8 pieces; piece p of tile row `key` is stored at position
+// p ^ swz(key). The XOR spreads the eight rows that one MFMA operand read
+// touches over distinct LDS banks, both for the 16-byte K reads and for the
+// 8-byte transposing V reads, without padding (direct HBM->LDS loads write
+// 1 KiB contiguous per wave instruction, so rows cannot be padded).
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (D == 128) return (key & 7) << 1;
+  else if constexpr (D == 64) return ((key >> 1) & 3) << 1;
+  else return ((key >> 2) & 1) << 1;
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane j receives element (j % 4) of the 8-byte rows addressed by
+// lanes 4e + j/4, e = 0..3, as its element e.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_byte_ptr) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_byte_ptr));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Row max / sum across the two half-waves (lanes l and l ^ 32 hold the same
+// query in the 32x32 accumulator layout).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// LAZY: keep a stale running max until some row's max has grown by more
+// than 2^8 (in exp2 units), so acc/l are rescaled only then. O and lse are
+// unchanged mathematically (exp(S - m) with any fixed m >= the values seen so
+// far minus 8 stays in [0, 256]). The split path keeps the exact chunk max
+// because it is part of the partial-state output.
 template <class E, int D, int BN, int NW, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(const FwdParams p) {
-  constexpr int NT = NW * 64;
+__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
   constexpr int BM = NW * 32;
-  constexpr int KP = D + 8;      // K tile row pitch (elements): spreads rows over banks
-  constexpr int VP = BN + 8;     // V^T tile row pitch (elements)
-  constexpr int KK = D / 16;     // MFMA k-steps of Q K^T
-  constexpr int KB = BN / 32;    // 32-key blocks per tile
-  constexpr int DB = D / 32;     // 32-wide d blocks of the output
-  constexpr int TPR = D / 8;     // 16-byte pieces per row
-  constexpr int KU = BN * TPR;   // K tile load units (one 16-byte piece each)
-  constexpr int VU = (BN / 4) * TPR;  // V tile load units (4 keys x 16 bytes each)
-  constexpr int KLOADS = (KU + NT - 1) / NT;
-  constexpr int VLOADS = (VU + NT - 1) / NT;
+  constexpr int PPR = D / 8;               // 16-byte pieces per row
+  constexpr int TILE_BYTES = BN * D * 2;   // one K or V tile
+  constexpr int NI = TILE_BYTES / 1024 / NW;  // 1 KiB direct loads per wave per tile
+  constexpr int KK = D / 16;               // MFMA k-steps of Q K^T
+  constexpr int KB = BN / 32;              // 32-key blocks per tile
+  constexpr int DB = D / 32;               // 32-wide d blocks of the output
+  constexpr bool LAZY = (MODE != MODE_SPLIT);
+  constexpr float LAZY_TH = 8.0f;
+  static_assert(NI >= 1 && TILE_BYTES % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VP];
+  // [buffer][K|V][tile]: double-buffered K and V tiles.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][BN * D];
 
   Work w;
   if (!decode_work<D, BM, CAUSAL, MODE>(p, w)) return;  // uniform over the workgroup
@@ -185,81 +225,55 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const FwdParams p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m = -INFINITY;  // running max, log2 units (score * scale * log2 e)
-  float l = 0.f;        // this lane's part of the rescaled exp-sum
+  float m = -INFINITY;  // running (possibly stale) max, log2 units
+  float l = 0.f;        // this lane's part of the exp-sum
 
   const int my_pos = w.q_pos0 + qrow;
   const int wave_first_pos = w.q_pos0 + wave * 32;
   const int wave_last_pos = wave_first_pos + 31;
   const bool wave_active = wave * 32 < w.nq;
   const float c = p.c;
-
   const int ntiles = (w.k_end - w.k_begin + BN - 1) / BN;
 
-  u32x4 kst[KLOADS];
-  u32x4 vst[VLOADS][4];
-
-  auto gload = [&](int t) {
+  // Direct HBM -> LDS tile load: slot s of the tile (16 bytes) holds piece
+  // (s % PPR) ^ swz(key) of tile row key = s / PPR. Keys past the end are
+  // clamped to the last valid key (their scores are masked to -inf).
+  auto issue_tile = [&](int t, int buf) {
     const int kbase = w.k_begin + t * BN;
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int u = tid + i * NT;
-      const int key = u / TPR, piece = u % TPR;
-      const int j = kbase + key;
-      kst[i] = (u < KU && j < w.k_end) ? *(const u32x4*)(w.k + (int64_t)j * w.kv_rs + piece * 8)
-                                       : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int u = tid + i * NT;
-      const int grp = u / TPR, piece = u % TPR;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = kbase + grp * 4 + r;
-        vst[i][r] = (u < VU && j < w.k_end)
-                        ? *(const u32x4*)(w.v + (int64_t)j * w.kv_rs + piece * 8)
-                        : u32x4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int s = (wave * NI + i) * 64 + lane;
+      const int key = s / PPR;
+      const int piece = (s % PPR) ^ swz<D>(key);
+      const int j = min(kbase + key, w.k_end - 1);
+      const int64_t off = (int64_t)j * w.kv_rs + piece * 8;
+      const int dst = (wave * NI + i) * 512;  // elements
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(w.k + off),
+                                       (__attribute__((address_space(3))) void*)(&smem[buf][0][dst]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(w.v + off),
+                                       (__attribute__((address_space(3))) void*)(&smem[buf][1][dst]), 16, 0, 0);
     }
   };
 
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int u = tid + i * NT;
-      if (u < KU) {
-        const int key = u / TPR, piece = u % TPR;
-        *(u32x4*)(sK + key * KP + piece * 8) = kst[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int u = tid + i * NT;
-      if (u < VU) {
-        const int grp = u / TPR, piece = u % TPR;
-        // 4 keys x 8 d -> 8 rows of V^T, 4 consecutive keys each.
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const int d = piece * 8 + wd * 2;
-          u32x2 even = {pack_lo16(vst[i][0][wd], vst[i][1][wd]), pack_lo16(vst[i][2][wd], vst[i][3][wd])};
-          u32x2 odd = {pack_hi16(vst[i][0][wd], vst[i][1][wd]), pack_hi16(vst[i][2][wd], vst[i][3][wd])};
-          *(u32x2*)(sV + d * VP + grp * 4) = even;
-          *(u32x2*)(sV + (d + 1) * VP + grp * 4) = odd;
-        }
-      }
-    }
-  };
+  // Per-lane LDS offsets (elements) that do not depend on the tile.
+  // K operand (A of S^T = K Q^T): row kb*32 + l32, piece kk*2 + hf.
+  // V operand (A of O^T = V^T P^T) via transposing reads: 16-lane group G
+  // covers d = db*32 + 16*(G&1) + 0..15 and keys base + 4*(G>>1) + 0..3.
+  const int g16 = lane >> 4;
+  const int tr_e = (lane & 15) >> 2;
+  const int tr_q = lane & 3;
 
-  if (ntiles > 0) gload(0);
+  if (ntiles > 0) issue_tile(0, 0);
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // every wave is done reading the previous tile
-    sstore();
-    __syncthreads();
-    if (t + 1 < ntiles) gload(t + 1);  // next tile's HBM reads overlap this tile's math
+    const int buf = t & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t visible to all waves; every wave is done with tile t-1
+    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
 
     const int kt0 = w.k_begin + t * BN;
-    const bool skip = !wave_active || (CAUSAL && kt0 > wave_last_pos);
-    if (skip) continue;
+    if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) continue;
+    const uint16_t* sK = smem[buf][0];
+    const uint16_t* sV = smem[buf][1];
 
     // ---- S^T = K Q^T for BN keys x 32 queries
     f32x16 s[KB];
@@ -267,9 +281,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const FwdParams p) {
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      const int key = kb * 32 + l32;
+      const int sw = swz<D>(key);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const u32x4 a = *(const u32x4*)(sK + (kb * 32 + l32) * KP + kk * 16 + hf * 8);
+        const int piece = (kk * 2 + hf) ^ sw;
+        const u32x4 a = *(const u32x4*)(sK + (key * PPR + piece) * 8);
         s[kb] = E::mfma32(a, qreg[kk], s[kb]);
       }
     }
@@ -283,8 +300,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool bad = (key >= w.k_end) || (CAUSAL && key > my_pos);
-          if (bad) s[kb][r] = -INFINITY;
+          if ((key >= w.k_end) || (CAUSAL && key > my_pos)) s[kb][r] = -INFINITY;
         }
     }
 
@@ -294,24 +310,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const FwdParams p) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, mx * c);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
+    mx = max_halves(mx);
+    const float m_cand = fmaxf(m, mx * c);
+    const bool need = LAZY ? (m_cand > m + LAZY_TH) : (m_cand > m);
+    // The branch is taken when any row of the wave needs a rescale, but each
+    // row applies only its own decision (alpha = 1 otherwise), so a row's bits
+    // never depend on other rows' data.
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float alpha = need ? fast_exp2(m - m_cand) : 1.0f;
+      m = need ? m_cand : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(fmaf(s[kb][r], c, -m_new));
+        const float pv = fast_exp2(fmaf(s[kb][r], c, -m));
         s[kb][r] = pv;
         rs += pv;
       }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    l += rs;
 
     // ---- O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
@@ -321,19 +344,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const FwdParams p) {
         const int o8 = half * 8;
         const u32x4 pb = {E::pack2(s[kb][o8 + 0], s[kb][o8 + 1]), E::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
                           E::pack2(s[kb][o8 + 4], s[kb][o8 + 5]), E::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
-        const int key0 = kb * 32 + half * 16 + 4 * hf;
+        const int key1 = kb * 32 + half * 16 + 4 * (g16 >> 1) + tr_e;
+        const int key2 = key1 + 8;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* vrow = sV + (db * 32 + l32) * VP + key0;
-          const u32x2 a0 = *(const u32x2*)(vrow);
-          const u32x2 a1 = *(const u32x2*)(vrow + 8);
+          const int d0 = db * 32 + 16 * (g16 & 1) + 4 * tr_q;
+          const int pc = d0 >> 3, within = d0 & 7;
+          const u32x2 a0 = lds_read_tr16(sV + (key1 * PPR + (pc ^ swz<D>(key1))) * 8 + within);
+          const u32x2 a1 = lds_read_tr16(sV + (key2 * PPR + (pc ^ swz<D>(key2))) * 8 + within);
           acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, acc[db]);
         }
       }
   }
 
   if (!wave_active) return;
-  const float lt = l + xor32(l);  // both halves of the wave hold partial sums of one query
+  const float lt = sum_halves(l);
 
   if constexpr (MODE != MODE_SPLIT) {
     if (!row_ok) return;

@@ -92,7 +92,7 @@ int launch_status() {
 // Query rows per workgroup (32 per wave) and keys per tile.
 template <int D, int MODE>
 struct Tile {
-  static constexpr int NW = (MODE == MODE_SPLIT) ? 1 : (D == 128 ? 4 : 2);
+  static constexpr int NW = D == 128 ? 4 : 2;
   static constexpr int BM = NW * 32;
   static constexpr int BN = 64;
 };

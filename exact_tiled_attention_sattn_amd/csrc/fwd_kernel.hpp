@@ -50,6 +50,7 @@ struct FwdParams {
   int nqt;         // query tiles per slice (dense/split) or per longest sequence (varlen)
   int nseq;        // varlen: S
   int total;       // varlen: T
+  int pair;        // dense causal: 1 = each workgroup takes query tiles (nqt-1-j, j)
   float c;         // scale * log2(e)
 };
 
@@ -68,14 +69,37 @@ struct Work {
   int64_t part_row0;   // split: index (slice_row * C + c) of row 0
 };
 
+// Spread of workgroups over the 8 XCDs: blocks are handed out round-robin by
+// block id, so remap the id to give XCD x one contiguous range of the
+// logical order (and with it whole heads, whose K/V then share one L2).
+__device__ __forceinline__ int xcd_linear(int bid) {
+  const int per = (int)(gridDim.x / 8);
+  return (bid < per * 8) ? (bid % 8) * per + bid / 8 : bid;
+}
+
+// Query tiles per workgroup: with enough workgroups to fill the chip, causal
+// dense workgroups take the pair (nqt-1-j, j), so every workgroup has the same
+// number of key tiles; small grids keep one tile each (shorter serial chain).
+template <bool CAUSAL, int MODE>
+constexpr int items_per_block() { return (MODE == MODE_DENSE && CAUSAL) ? 2 : 1; }
+
 template <int D, int BM, bool CAUSAL, int MODE>
-__device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
+__device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& w) {
   const int bid = blockIdx.x;
   if constexpr (MODE == MODE_DENSE) {
-    // Heaviest query tiles first (they have the most key tiles when causal);
-    // consecutive block ids are different heads of the same query tile.
-    const int qt = p.nqt - 1 - bid / p.heads;
-    const int head = bid % p.heads;
+    const int lin = xcd_linear(bid);
+    int head, qt;
+    if (CAUSAL && p.pair) {
+      const int npairs = (p.nqt + 1) / 2;
+      head = lin / npairs;
+      const int j = lin % npairs;
+      qt = (item == 0) ? p.nqt - 1 - j : j;
+      if (item == 1 && qt == p.nqt - 1 - j) return false;  // odd count: middle tile once
+    } else {
+      if (item > 0) return false;
+      head = lin / p.nqt;
+      qt = p.nqt - 1 - lin % p.nqt;
+    }
     const int64_t base = (int64_t)head * p.n * D;
     w.q_pos0 = qt * BM;
     w.nq = min(BM, p.n - w.q_pos0);
@@ -90,11 +114,15 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
     w.k_end = CAUSAL ? min(p.n, w.q_pos0 + BM) : p.n;
     return w.nq > 0;
   } else if constexpr (MODE == MODE_VARLEN) {
+    // Heaviest query tiles first over all sequences; within one tile index
+    // and sequence, the Hq query heads are permuted so that the heads sharing
+    // a KV head sit on the same XCD (block id mod 8).
     const int per_tile = p.nseq * p.hq;
     const int qt = p.nqt - 1 - bid / per_tile;
     const int rem = bid % per_tile;
     const int s = rem / p.hq;
-    const int h = rem % p.hq;
+    const int j = rem % p.hq;
+    const int h = (p.hq % 8 == 0) ? (j % 8) * (p.hq / 8) + j / 8 : j;
     // Clamp the table so that a malformed one cannot address outside [0, T).
     int a = p.cu_seqlens[s];
     int b = p.cu_seqlens[s + 1];
@@ -143,15 +171,22 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, Work& w) {
 
 // 16-byte piece swizzle of a K/V tile row in LDS. A row of D bf16/fp16
 // values is PPR = D/8 pieces; piece p of tile row `key` is stored at position
-// p ^ swz(key). The XOR spreads the eight rows that one MFMA operand read
-// touches over distinct LDS banks, both for the 16-byte K reads and for the
-// 8-byte transposing V reads, without padding (direct HBM->LDS loads write
-// 1 KiB contiguous per wave instruction, so rows cannot be padded).
+// p ^ swz(key). LDS serves 256 bytes (64 banks x 4 bytes) per clock: 16 lanes
+// of a 16-byte read, 32 lanes of an 8-byte read. swz makes both operand reads
+// conflict-free:
+//   * K (A of S^T = K Q^T): 16 lanes read one piece of 16 consecutive rows;
+//     their positions must be distinct within the 256-byte bank window.
+//   * V (transposing 8-byte reads): 32 lanes read 4 pieces of 4 consecutive
+//     rows; the four rows' piece groups must land on different banks.
+// Direct HBM->LDS loads write 1 KiB contiguous per wave instruction, so rows
+// cannot be padded; the permutation does the spreading instead. swz(key)
+// depends only on key mod 16, and on nothing that changes between 32-row
+// blocks, so per-lane operand offsets are tile independent.
 template <int D>
 __device__ __forceinline__ int swz(int key) {
-  if constexpr (D == 128) return (key & 7) << 1;
-  else if constexpr (D == 64) return ((key >> 1) & 3) << 1;
-  else return ((key >> 2) & 1) << 1;
+  if constexpr (D == 128) return ((key & 3) << 2) | ((key >> 2) & 3);   // 16 pieces: swap 2-bit halves
+  else if constexpr (D == 64) return ((key >> 1) & 1) << 2 | ((key >> 2) & 3);  // 8 pieces
+  else return (key >> 2) & 3;                                          // 4 pieces
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -178,14 +213,14 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// LAZY: keep a stale running max until some row's max has grown by more
-// than 2^8 (in exp2 units), so acc/l are rescaled only then. O and lse are
-// unchanged mathematically (exp(S - m) with any fixed m >= the values seen so
-// far minus 8 stays in [0, 256]). The split path keeps the exact chunk max
-// because it is part of the partial-state output.
+// One query tile of BM = 32*NW rows against the keys [k_begin, k_end) of its
+// slice. LAZY: keep a stale running max until some row's max has grown by
+// more than 2^8 (in exp2 units), so acc/l are rescaled only then. O and lse
+// are unchanged mathematically (exp(S - m) with any fixed m >= the values
+// seen so far minus 8 stays in [0, 256]). The split path keeps the exact
+// chunk max because it is part of the partial-state output.
 template <class E, int D, int BN, int NW, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
-  constexpr int BM = NW * 32;
+__device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uint16_t* sbuf0, uint16_t* sbuf1) {
   constexpr int PPR = D / 8;               // 16-byte pieces per row
   constexpr int TILE_BYTES = BN * D * 2;   // one K or V tile
   constexpr int NI = TILE_BYTES / 1024 / NW;  // 1 KiB direct loads per wave per tile
@@ -197,15 +232,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
   static_assert(NI >= 1 && TILE_BYTES % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
 
-  // [buffer][K|V][tile]: double-buffered K and V tiles.
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][BN * D];
-
-  Work w;
-  if (!decode_work<D, BM, CAUSAL, MODE>(p, w)) return;  // uniform over the workgroup
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -235,60 +265,80 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
   const float c = p.c;
   const int ntiles = (w.k_end - w.k_begin + BN - 1) / BN;
 
-  // Direct HBM -> LDS tile load: slot s of the tile (16 bytes) holds piece
-  // (s % PPR) ^ swz(key) of tile row key = s / PPR. Keys past the end are
-  // clamped to the last valid key (their scores are masked to -inf).
-  auto issue_tile = [&](int t, int buf) {
-    const int kbase = w.k_begin + t * BN;
+  // Tile loads: buffer loads straight into LDS. The descriptors cover keys
+  // [0, k_end) of the slice, so reads past the last key return zeros. Slot
+  // s of a tile (16 bytes) holds piece (s % PPR) ^ swz(key) of tile row
+  // key = s / PPR; the per-lane byte offsets do not depend on the tile.
+  const uint32_t row_bytes = (uint32_t)w.kv_rs * 2u;
+  const uint32_t span = (uint32_t)w.k_end * row_bytes;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)w.k, (short)0, (int)span, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)w.v, (short)0, (int)span, 0x00020000);
+  uint32_t voff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = (wave * NI + i) * 64 + lane;
+    const int key = slot / PPR;
+    voff[i] = (uint32_t)key * row_bytes + (uint32_t)(((slot % PPR) ^ swz<D>(key)) * 16);
+  }
+  auto issue_tile = [&](int t, uint16_t* sb) {
+    const uint32_t soff = (uint32_t)(w.k_begin + t * BN) * row_bytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int s = (wave * NI + i) * 64 + lane;
-      const int key = s / PPR;
-      const int piece = (s % PPR) ^ swz<D>(key);
-      const int j = min(kbase + key, w.k_end - 1);
-      const int64_t off = (int64_t)j * w.kv_rs + piece * 8;
-      const int dst = (wave * NI + i) * 512;  // elements
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(w.k + off),
-                                       (__attribute__((address_space(3))) void*)(&smem[buf][0][dst]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(w.v + off),
-                                       (__attribute__((address_space(3))) void*)(&smem[buf][1][dst]), 16, 0, 0);
+      uint16_t* dst = sb + (wave_u * NI + i) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst), 16, voff[i],
+                                               soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dst + BN * D), 16,
+                                               voff[i], soff, 0, 0);
     }
   };
 
-  // Per-lane LDS offsets (elements) that do not depend on the tile.
-  // K operand (A of S^T = K Q^T): row kb*32 + l32, piece kk*2 + hf.
-  // V operand (A of O^T = V^T P^T) via transposing reads: 16-lane group G
-  // covers d = db*32 + 16*(G&1) + 0..15 and keys base + 4*(G>>1) + 0..3.
+  // Per-lane LDS element offsets of the MFMA A operands (tile independent).
+  // K: tile row kb*32 + l32, piece 2*kk + hf (swizzle depends on l32 only).
+  int kofs[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) kofs[kk] = l32 * D + (((kk * 2 + hf) ^ swz<D>(l32)) * 8);
+  // V via transposing reads: 16-lane group G covers d = db*32 + 16*(G&1) +
+  // 0..15 and keys base + 4*(G>>1) + 0..3; lane supplies the 8-byte row
+  // piece of key (lane&15)>>2 at d offset 4*(lane&3).
+  // The two reads of one operand cover rows tr_key and tr_key + 8 of a
+  // 16-row group; their swizzles differ, so each has its own offsets.
   const int g16 = lane >> 4;
-  const int tr_e = (lane & 15) >> 2;
-  const int tr_q = lane & 3;
+  const int tr_key = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+  int vofs[2][DB];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = db * 32 + 16 * (g16 & 1) + 4 * (lane & 3);
+      const int key = tr_key + 8 * x;
+      vofs[x][db] = key * D + (((d0 >> 3) ^ swz<D>(key)) * 8) + (d0 & 7);
+    }
 
-  if (ntiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // One tile: wait for its loads, start the next tile's loads into the other
+  // buffer, then compute on this one.
+  auto step = [&](int t, const uint16_t* cur, uint16_t* nxt) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile t visible to all waves; every wave is done with tile t-1
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    if (t + 1 < ntiles) issue_tile(t + 1, nxt);
 
     const int kt0 = w.k_begin + t * BN;
-    if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) continue;
-    const uint16_t* sK = smem[buf][0];
-    const uint16_t* sV = smem[buf][1];
+    if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
+    const uint16_t* sK = cur;
+    const uint16_t* sV = cur + BN * D;
 
-    // ---- S^T = K Q^T for BN keys x 32 queries
+    // ---- S^T = K Q^T for BN keys x 32 queries (all K operands read first)
+    u32x4 ka[KB][KK];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) ka[kb][kk] = *(const u32x4*)(sK + kofs[kk] + kb * 32 * D);
     f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int key = kb * 32 + l32;
-      const int sw = swz<D>(key);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int piece = (kk * 2 + hf) ^ sw;
-        const u32x4 a = *(const u32x4*)(sK + (key * PPR + piece) * 8);
-        s[kb] = E::mfma32(a, qreg[kk], s[kb]);
-      }
+      for (int kk = 0; kk < KK; ++kk) s[kb] = E::mfma32(ka[kb][kk], qreg[kk], s[kb]);
     }
 
     // ---- mask: key tail, and keys after the query (diagonal kept)
@@ -344,17 +394,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
         const int o8 = half * 8;
         const u32x4 pb = {E::pack2(s[kb][o8 + 0], s[kb][o8 + 1]), E::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
                           E::pack2(s[kb][o8 + 4], s[kb][o8 + 5]), E::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
-        const int key1 = kb * 32 + half * 16 + 4 * (g16 >> 1) + tr_e;
-        const int key2 = key1 + 8;
+        const int krow = (kb * 32 + half * 16) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d0 = db * 32 + 16 * (g16 & 1) + 4 * tr_q;
-          const int pc = d0 >> 3, within = d0 & 7;
-          const u32x2 a0 = lds_read_tr16(sV + (key1 * PPR + (pc ^ swz<D>(key1))) * 8 + within);
-          const u32x2 a1 = lds_read_tr16(sV + (key2 * PPR + (pc ^ swz<D>(key2))) * 8 + within);
+          const u32x2 a0 = lds_read_tr16(sV + vofs[0][db] + krow);
+          const u32x2 a1 = lds_read_tr16(sV + vofs[1][db] + krow);
           acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, acc[db]);
         }
       }
+  };
+
+  if (ntiles > 0) issue_tile(0, sbuf0);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sbuf0, sbuf1);
+    if (t + 1 < ntiles) step(t + 1, sbuf1, sbuf0);
   }
 
   if (!wave_active) return;
@@ -390,6 +443,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
       p.part_m[prow] = m * kLn2;  // natural-log units of the scaled score
       p.part_l[prow] = lt;
     }
+  }
+}
+
+template <class E, int D, int BN, int NW, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
+  constexpr int BM = NW * 32;
+  // Double-buffered K and V tiles, as two distinct arrays so the compiler can
+  // tell that reads of one buffer never alias the prefetch into the other
+  // (otherwise it makes every LDS read wait for the in-flight prefetch).
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[2 * BN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[2 * BN * D];
+  constexpr int NITEMS = items_per_block<CAUSAL, MODE>();
+#pragma unroll 1
+  for (int item = 0; item < NITEMS; ++item) {
+    if (item > 0) __syncthreads();  // the previous tile's LDS reads are done
+    Work w;
+    if (!decode_work<D, BM, CAUSAL, MODE>(p, item, w)) continue;  // uniform over the workgroup
+    attn_rows<E, D, BN, NW, CAUSAL, MODE>(p, w, sbuf0, sbuf1);
   }
 }
 

@@ -33,6 +33,9 @@ int ok() {
 
 // Positions inside one sequence or slice are kept in 32-bit registers.
 constexpr int64_t kMaxLen = int64_t(1) << 30;
+// K/V tiles are fetched with buffer loads whose byte offset within one slice
+// (or one packed sequence) is 32-bit.
+constexpr int64_t kMaxSpan = int64_t(1) << 31;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
@@ -183,9 +186,13 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
   Range outs[2] = {range_of(o, bytes, "o"), range_of(lse, rows * 4, "lse")};
   if ((st = check_alias(ins, 3, outs, 2))) return st;
 
+  if (N * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
   const int bm = tile_m<MODE_DENSE>(D);
   const int64_t nqt = (N + bm - 1) / bm;
-  const int64_t grid = nqt * heads;
+  // Causal workgroups take a pair of query tiles (equal work per workgroup)
+  // once there are at least two workgroups per CU's two slots.
+  const bool pair = causal && nqt * heads >= 1024;
+  const int64_t grid = (pair ? (nqt + 1) / 2 : nqt) * heads;
   if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
   FwdParams p = blank_params(scale);
   p.q = (const uint16_t*)q;
@@ -196,6 +203,7 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
   p.heads = (int)heads;
   p.n = (int)N;
   p.nqt = (int)nqt;
+  p.pair = pair ? 1 : 0;
   dispatch_fwd<MODE_DENSE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
   return launch_status();
 }
@@ -215,6 +223,7 @@ int sattn_fwd_split(int dtype, const void* q, const void* k, const void* v, floa
   if (qrows == 0) return ok();
   if (Nk == 0) return fail(SATTN_ERR_SHAPE, "Nk must be > 0 (a row with no keys has no partials)");
   if (Nq >= kMaxLen || Nk >= kMaxLen || B * Hq >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "size too large");
+  if (Nk * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
   const int64_t C = (Nk + chunk - 1) / chunk;
   int64_t prow, mbytes, abytes;
   if (!product({qrows, C}, &prow) || !product({prow, 4}, &mbytes) || !product({prow, D, 4}, &abytes))
@@ -299,6 +308,7 @@ int sattn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, voi
   if (S == 0 || T == 0 || Hq == 0 || max_seqlen == 0) return ok();
   if (T >= kMaxLen || S >= kMaxLen || Hq >= 65536 || max_seqlen > T)
     return fail(max_seqlen > T ? SATTN_ERR_SHAPE : SATTN_ERR_UNSUPPORTED, "max_seqlen > T or size too large");
+  if (max_seqlen * Hkv * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "a sequence's K/V span exceeds 2 GiB");
   if (!q || !k || !v || !o || !lse || !cu_seqlens) return fail(SATTN_ERR_NULL, "null pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
       !aligned(cu_seqlens, 4))

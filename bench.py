@@ -266,9 +266,10 @@ def cpu_baseline(budget_s):
     except OSError:
         pass
     return {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "numpy float64 dense oracle on %d sampled query rows (64 per head, both causal and noncausal "
-                      "variants, all 4096 keys) of the 4x16x4096x128 workload in %.1f s; scaled by the sampled "
-                      "fraction of rows (%.5f)" % (rows_done, el, frac),
+            "sample": "numpy float64 dense oracle on %d seeded query rows (64 per head per draw, heads in turn; each "
+                      "row against all 4096 keys, computed both noncausal and causal) of the 4x16x4096x128 workload "
+                      "in %.1f s; that is %.3f times the query rows of one step, and value = that share of one "
+                      "step's FLOPs / time" % (rows_done, el, frac),
             "host_cores_visible": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
 
 

@@ -37,6 +37,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 KERNEL_SOURCES = ["exact_tiled_attention_sattn_amd/csrc/fwd_kernel.hpp",
                   "exact_tiled_attention_sattn_amd/csrc/common.hpp",
+                  "exact_tiled_attention_sattn_amd/csrc/fwd_small.hpp",
                   "exact_tiled_attention_sattn_amd/csrc/sattn.hip"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_kernel_batched_4x16x4096x128_bf16_pmc.json")
 DEV = "cuda:0"

@@ -11,6 +11,7 @@
 
 #include "../../include/sattn.h"
 #include "fwd_kernel.hpp"
+#include "fwd_small.hpp"
 
 namespace {
 
@@ -187,6 +188,39 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
   if ((st = check_alias(ins, 3, outs, 2))) return st;
 
   if (N * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
+  // Small problems (at most one workgroup of 32 rows per CU): split each
+  // head's keys between the waves of a workgroup to shorten the serial chain.
+  const int64_t nq32 = (N + 31) / 32;
+  if (D <= 64 && heads * nq32 <= 256) {
+    FwdParams p = blank_params(scale);
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.o = (uint16_t*)o;
+    p.lse = lse;
+    p.heads = (int)heads;
+    p.n = (int)N;
+    p.nqt = (int)nq32;
+    hipStream_t s = (hipStream_t)stream;
+    // 8 waves when a query tile may see more than 4 key tiles, else 4.
+    const bool wide = (N + 63) / 64 > 4;
+    const dim3 g((unsigned)(heads * nq32)), b(wide ? 512 : 256);
+#define SATTN_SMALL(E_, D_) \
+  if (wide) { \
+    if (causal) hipLaunchKernelGGL((fwd_small_kernel<E_, D_, 8, true>), g, b, 0, s, p); \
+    else hipLaunchKernelGGL((fwd_small_kernel<E_, D_, 8, false>), g, b, 0, s, p); \
+  } else { \
+    if (causal) hipLaunchKernelGGL((fwd_small_kernel<E_, D_, 4, true>), g, b, 0, s, p); \
+    else hipLaunchKernelGGL((fwd_small_kernel<E_, D_, 4, false>), g, b, 0, s, p); \
+  }
+    if (dtype == SATTN_BF16) {
+      if (D == 32) { SATTN_SMALL(Bf16, 32) } else { SATTN_SMALL(Bf16, 64) }
+    } else {
+      if (D == 32) { SATTN_SMALL(F16, 32) } else { SATTN_SMALL(F16, 64) }
+    }
+#undef SATTN_SMALL
+    return launch_status();
+  }
   const int bm = tile_m<MODE_DENSE>(D);
   const int64_t nqt = (N + bm - 1) / bm;
   // Causal workgroups take a pair of query tiles (equal work per workgroup)

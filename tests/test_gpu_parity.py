@@ -44,6 +44,9 @@ SMALL = [
     (1, 1, 1, 32, "fp16"), (1, 1, 2, 64, "bf16"), (1, 2, 31, 128, "bf16"), (2, 3, 65, 32, "fp16"),
     (1, 2, 127, 64, "bf16"), (1, 1, 129, 128, "fp16"), (2, 2, 200, 64, "fp16"), (1, 3, 333, 128, "bf16"),
     (1, 1, 257, 32, "bf16"), (1, 2, 513, 128, "fp16"),
+    # many heads: D <= 64 problems that take the streaming kernel rather than
+    # the small-problem kernel (more than 256 workgroups of 32 rows)
+    (4, 16, 300, 64, "fp16"), (2, 40, 200, 32, "bf16"),
 ]
 
 

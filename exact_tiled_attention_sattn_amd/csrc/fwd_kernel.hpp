@@ -114,15 +114,19 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.k_end = CAUSAL ? min(p.n, w.q_pos0 + BM) : p.n;
     return w.nq > 0;
   } else if constexpr (MODE == MODE_VARLEN) {
-    // Heaviest query tiles first over all sequences; within one tile index
-    // and sequence, the Hq query heads are permuted so that the heads sharing
-    // a KV head sit on the same XCD (block id mod 8).
-    const int per_tile = p.nseq * p.hq;
-    const int qt = p.nqt - 1 - bid / per_tile;
-    const int rem = bid % per_tile;
-    const int s = rem / p.hq;
-    const int j = rem % p.hq;
-    const int h = (p.hq % 8 == 0) ? (j % 8) * (p.hq / 8) + j / 8 : j;
+    // Logical order: KV head, then sequence, then query tile (heaviest
+    // first), then the query heads sharing that KV head; each XCD receives a
+    // contiguous range of it, so the workgroups reading one sequence's K/V of
+    // one KV head run together on one L2.
+    const int grp = p.hq / p.hkv;
+    const int lin = xcd_linear(bid);
+    const int per_g = p.nseq * p.nqt * grp;
+    const int g_kv = lin / per_g;
+    const int r1 = lin % per_g;
+    const int s = r1 / (p.nqt * grp);
+    const int r2 = r1 % (p.nqt * grp);
+    const int qt = p.nqt - 1 - r2 / grp;
+    const int h = g_kv * grp + r2 % grp;
     // Clamp the table so that a malformed one cannot address outside [0, T).
     int a = p.cu_seqlens[s];
     int b = p.cu_seqlens[s + 1];

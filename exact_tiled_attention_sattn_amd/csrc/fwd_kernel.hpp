@@ -318,9 +318,25 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
       vofs[x][db] = key * D + (((d0 >> 3) ^ swz<D>(key)) * 8) + (d0 & 7);
     }
 
+  // Two ways to keep the softmax state of a row across tiles:
+  //  * exact online update: running max, acc/l rescaled when the max grows
+  //    (lazily, by more than 2^8 in exp2 units outside the split path);
+  //  * fixed reference (FAST): the row's max over the first tile is kept as m
+  //    for all later tiles, which then need no max and no rescale at all:
+  //    p = exp2(S*c - m). O and lse do not depend on which m is used as long
+  //    as nothing overflows; with every tile sum <= 2^64, l <= 2^94 and
+  //    acc <= 2^110 for any N < 2^30 and |v| < 2^16. A row whose tile sum
+  //    exceeds 2^64 (or is not finite) raises `overflow`; if any row of the
+  //    workgroup did, the workgroup recomputes its rows with the exact online
+  //    update (a data-dependent slow path; random inputs never take it).
+  bool overflow = false;
+  constexpr float FAST_LIMIT = 18446744073709551616.0f;  // 2^64
+
   // One tile: wait for its loads, start the next tile's loads into the other
   // buffer, then compute on this one.
-  auto step = [&](int t, const uint16_t* cur, uint16_t* nxt) {
+  auto step = [&](int t, const uint16_t* cur, uint16_t* nxt, auto mask_tag, auto fast_tag) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
+    constexpr bool FAST = decltype(fast_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile t visible to all waves; every wave is done with tile t-1
     if (t + 1 < ntiles) issue_tile(t + 1, nxt);
@@ -346,9 +362,7 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
     }
 
     // ---- mask: key tail, and keys after the query (diagonal kept)
-    const bool tail = kt0 + BN > w.k_end;
-    const bool diag = CAUSAL && (kt0 + BN - 1 > wave_first_pos);
-    if (tail || diag) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -358,37 +372,52 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
         }
     }
 
-    // ---- online softmax update (fp32)
-    float mx = -INFINITY;
+    if constexpr (FAST) {
+      // ---- fixed-reference update: exps against the row's first-tile max
+      float rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_halves(mx);
-    const float m_cand = fmaxf(m, mx * c);
-    const bool need = LAZY ? (m_cand > m + LAZY_TH) : (m_cand > m);
-    // The branch is taken when any row of the wave needs a rescale, but each
-    // row applies only its own decision (alpha = 1 otherwise), so a row's bits
-    // never depend on other rows' data.
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float alpha = need ? fast_exp2(m - m_cand) : 1.0f;
-      m = need ? m_cand : m;
-      l *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(fmaf(s[kb][r], c, -m));
+          s[kb][r] = pv;
+          rs += pv;
+        }
+      l += rs;
+      overflow = overflow || !(rs <= FAST_LIMIT);
+    } else {
+      // ---- exact online update (fp32)
+      float mx = -INFINITY;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    }
-    float rs = 0.f;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = max_halves(mx);
+      const float m_cand = fmaxf(m, mx * c);
+      const bool need = LAZY ? (m_cand > m + LAZY_TH) : (m_cand > m);
+      // The branch is taken when any row of the wave needs a rescale, but
+      // each row applies only its own decision (alpha = 1 otherwise), so a
+      // row's bits never depend on other rows' data.
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = need ? fast_exp2(m - m_cand) : 1.0f;
+        m = need ? m_cand : m;
+        l *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(fmaf(s[kb][r], c, -m));
-        s[kb][r] = pv;
-        rs += pv;
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       }
-    l += rs;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(fmaf(s[kb][r], c, -m));
+          s[kb][r] = pv;
+          rs += pv;
+        }
+      l += rs;
+    }
 
     // ---- O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
@@ -408,10 +437,41 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
       }
   };
 
-  if (ntiles > 0) issue_tile(0, sbuf0);
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sbuf0, sbuf1);
-    if (t + 1 < ntiles) step(t + 1, sbuf1, sbuf0);
+  // Tiles [0, n_full) need no mask for any row of the workgroup (they end
+  // before its first query and before the key tail); the rest take the masked
+  // body. Tile 0 always takes the exact update: it sets each row's max.
+  int n_full = (w.k_end - w.k_begin) / BN;
+  if (CAUSAL) n_full = min(n_full, max(0, (w.q_pos0 - w.k_begin + 1) / BN));
+  const std::integral_constant<bool, false> no{};
+  const std::integral_constant<bool, true> yes{};
+  auto run = [&](auto fast_tag) {
+    if (ntiles == 0) return;
+    issue_tile(0, sbuf0);
+    if (n_full >= 1) step(0, sbuf0, sbuf1, no, no);
+    else step(0, sbuf0, sbuf1, yes, no);
+    int t = 1;
+    for (; t + 1 < n_full; t += 2) {
+      step(t, sbuf1, sbuf0, no, fast_tag);
+      step(t + 1, sbuf0, sbuf1, no, fast_tag);
+    }
+    for (; t < ntiles; ++t) {
+      if (t & 1) step(t, sbuf1, sbuf0, yes, fast_tag);
+      else step(t, sbuf0, sbuf1, yes, fast_tag);
+    }
+  };
+  if constexpr (MODE == MODE_SPLIT) {
+    run(no);  // the partial state exports the exact chunk max
+  } else {
+    run(yes);
+    if (__syncthreads_or(overflow ? 1 : 0)) {  // rare: redo with the exact update
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+      m = -INFINITY;
+      l = 0.f;
+      run(no);
+    }
   }
 
   if (!wave_active) return;

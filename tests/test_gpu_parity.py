@@ -356,3 +356,48 @@ def test_varlen_bad_table_rejected_by_binding():
     bad = torch.tensor([0, 12, 20], dtype=torch.int32)
     with pytest.raises(ValueError):
         sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), bad, max_seqlen=10)
+
+
+# ------------------------------------------------- fixed-reference fast path
+def _growth_inputs(n, d, dt, jump, seed):
+    """q = 1; k_j constant along d: 0 for the first 64 keys, `jump` after, so
+    every row's score grows by sqrt(D)*jump after the first key tile."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.ones((1, 2, n, d), dtype=W.DTYPES[dt])
+    k = torch.zeros((1, 2, n, d), dtype=torch.float32)
+    k[:, :, 64:, :] = jump
+    k = k.to(W.DTYPES[dt])
+    v = torch.randn((1, 2, n, d), generator=g).to(W.DTYPES[dt])
+    return q, k, v
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("jump", [3.0, 50.0])
+def test_score_growth_after_first_tile(causal, jump):
+    """jump 3: scores grow by ~2^49 in exp2 units (absorbed by the fixed
+    reference); jump 50: the tile sums overflow and the workgroup takes the
+    exact online update instead. Both must match the oracle."""
+    _banner("growth", causal, jump)
+    n, d = 300, 128
+    q, k, v = _growth_inputs(n, d, "bf16", jump, seed=21)
+    scale = W.scale_f32(d)
+    o, lse = _run_fwd(q, k, v, causal, scale)
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "growth")
+
+
+def test_score_growth_varlen_fallback():
+    _banner("growth varlen")
+    lengths = [200, 130]
+    t = sum(lengths)
+    g = torch.Generator().manual_seed(22)
+    q = torch.ones((t, 4, 128), dtype=torch.bfloat16)
+    k = torch.zeros((t, 2, 128), dtype=torch.float32)
+    k[64:200] = 50.0            # first sequence: huge growth after its first tile
+    k = k.to(torch.bfloat16)
+    v = torch.randn((t, 2, 128), generator=g).to(torch.bfloat16)
+    cu = W.cu_seqlens_of(lengths)
+    o, lse = sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(cu), causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.varlen_gqa(W.to_f64(q), W.to_f64(k), W.to_f64(v), cu, W.scale_f32(128), True)
+    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "growth varlen")

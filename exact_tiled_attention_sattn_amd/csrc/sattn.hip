@@ -93,10 +93,14 @@ int launch_status() {
 }
 
 // ---------------------------------------------------------------- tiles
-// Query rows per workgroup (32 per wave) and keys per tile.
+// Query rows per workgroup (32 per wave) and keys per tile. Dense D = 128
+// runs 8 waves (256 query rows) per workgroup, one workgroup per CU: each K/V
+// tile staged in LDS then serves twice as many queries as with 4 waves, and
+// every SIMD still holds two waves. Varlen and split keep 4 waves, whose
+// 128-row granularity wastes fewer rows on short sequences and few queries.
 template <int D, int MODE>
 struct Tile {
-  static constexpr int NW = D == 128 ? 4 : 2;
+  static constexpr int NW = D == 128 ? (MODE == MODE_DENSE ? 8 : 4) : 2;
   static constexpr int BM = NW * 32;
   static constexpr int BN = 64;
 };
@@ -224,7 +228,8 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
   const int bm = tile_m<MODE_DENSE>(D);
   const int64_t nqt = (N + bm - 1) / bm;
   // Causal workgroups take a pair of query tiles (equal work per workgroup)
-  // once there are at least two workgroups per CU's two slots.
+  // once the grid has enough tiles that pairing still leaves several
+  // workgroups per CU.
   const bool pair = causal && nqt * heads >= 1024;
   const int64_t grid = (pair ? (nqt + 1) / 2 : nqt) * heads;
   if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");

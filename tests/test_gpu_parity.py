@@ -101,6 +101,33 @@ def test_c3_batched_4x16x4096x128_bf16_sampled(causal):
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
+# Causal grids large enough that workgroups take query-tile pairs (j,
+# nqt-1-j), with an odd tile count (the middle tile runs once) and a ragged
+# last tile: 256-row tiles at D = 128, 64-row tiles at D = 64.
+PAIRED = [(1, 205, 1270, 128, "bf16"), (1, 34, 1940, 64, "fp16")]
+
+
+@pytest.mark.parametrize("b,h,n,d,dt", PAIRED)
+def test_causal_paired_tiles_sampled(b, h, n, d, dt):
+    _banner("paired causal", b, h, n, d, dt)
+    seed = 4000 + n
+    q, k, v = _dense_inputs(b, h, n, d, dt, seed)
+    scale = W.scale_f32(d)
+    o, lse = _run_fwd(q, k, v, True, scale)
+    rows = W.sample_rows(seed, n, 24, groups=b * h).reshape(b, h, -1)
+    # rows around tile edges too: the middle tile and the last (ragged) one
+    edge = np.array([0, 255, 256, 511, 512, 767, 768, 1023, 1024, n - 2, n - 1])
+    edge = edge[edge < n]
+    rows = np.sort(np.concatenate([rows, np.broadcast_to(edge, (b, h, edge.size))], axis=2), axis=2)
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, True, rows=rows)
+    idx = torch.from_numpy(rows)
+    oc, lc = o.cpu(), lse.cpu()
+    o_s = torch.stack([torch.stack([oc[i, j][idx[i, j]] for j in range(h)]) for i in range(b)])
+    lse_s = torch.stack([torch.stack([lc[i, j][idx[i, j]] for j in range(h)]) for i in range(b)])
+    check_attention(o_s, lse_s, o_ref, lse_ref, W.DTYPES[dt], "paired causal")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
 # ------------------------------------------------------- closed form on GPU
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
 def test_zero_q_gives_mean_of_values(dt):

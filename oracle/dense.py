@@ -128,30 +128,79 @@ def varlen_gqa(q, k, v, cu_seqlens, scale, causal=True, rows=None):
     return o, lse
 
 
-def split_partials(q, k, v, scale, chunk):
-    """Unnormalized per-chunk partial states of non-causal attention.
+def cache_positions(nq, nk):
+    """Logical positions of Nq queries that are the last Nq tokens of a
+    sequence whose keys/values (the cache) hold Nk positions: query i sits at
+    i + (Nk - Nq) (bottom-right alignment). Lesson 04 of "Attention
+    algorithms and data movement" asks for unequal-length alignment derived
+    from logical positions but prints no rule; this is the reading used here.
+    With Nq > Nk the first Nq - Nk queries sit before position 0."""
+    return np.arange(nq, dtype=np.int64) + (nk - nq)
+
+
+def attention_cache(q, k, v, scale, causal=False, rows=None):
+    """Queries against a key/value cache of another length, grouped heads.
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D]. Query head h reads KV head
+    h // (Hq / Hkv) (lesson 05, GQA head mapping; the cache holds Hkv heads).
+    Causal eligibility: key j is eligible for query i iff
+    j <= i + (Nk - Nq) (``cache_positions``); a query with no eligible key is
+    the empty row (O = 0, lse = -inf). Non-causal queries see all Nk keys.
+    ``rows``: optional int array [B, Hq, R] of query indices; then only those
+    rows are computed. Returns o [B, Hq, Nq or R, Dv] and lse [B, Hq, Nq or R].
+    """
+    b_, hq, nq = q.shape[0], q.shape[1], q.shape[2]
+    hkv, nk = k.shape[1], k.shape[2]
+    assert hq % hkv == 0
+    group = hq // hkv
+    pos = cache_positions(nq, nk)
+    r_count = nq if rows is None else np.asarray(rows).shape[2]
+    o = np.zeros((b_, hq, r_count, v.shape[3]), dtype=np.float64)
+    lse = np.full((b_, hq, r_count), NEG_INF, dtype=np.float64)
+    for b in range(b_):
+        for h in range(hq):
+            g = h // group
+            r = np.arange(nq) if rows is None else np.asarray(rows)[b, h]
+            o[b, h], lse[b, h] = attention(q[b, h][r], k[b, g], v[b, g], scale, causal, q_pos=pos[r])
+    return o, lse
+
+
+def split_partials(q, k, v, scale, chunk, causal=False, q_pos=None):
+    """Unnormalized per-chunk partial states of attention.
 
     Keys are split into consecutive chunks [c*chunk, min(Nk, (c+1)*chunk)).
     For each query row i and chunk c (the partial-statistics stage of the
     split structure in "Intermediate and advanced extension", workshop table,
-    split-softmax row, applied to attention):
+    split-softmax row, applied to attention), over the eligible keys j of c:
 
         m_ic   = max_{j in c} S_ij
         l_ic   = sum_{j in c} exp(S_ij - m_ic)
         acc_ic = sum_{j in c} exp(S_ij - m_ic) v_j       (not divided by l)
 
+    Causal: key j is eligible for row i iff j <= q_pos[i] (q_pos defaults to
+    ``cache_positions(Nq, Nk)``). A chunk with no eligible key for a row gives
+    that row the empty state m = -inf, l = 0, acc = 0 (lesson 01: the
+    explicit identity of the merge).
+
     q: [Nq, D], k, v: [Nk, D]. Returns m [Nq, C], l [Nq, C], acc [Nq, C, Dv].
     """
     nq, nk = q.shape[0], k.shape[0]
     nchunk = -(-nk // chunk)
+    if q_pos is None:
+        q_pos = cache_positions(nq, nk)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
     m = np.full((nq, nchunk), NEG_INF)
     l = np.zeros((nq, nchunk))
     acc = np.zeros((nq, nchunk, v.shape[1]))
     for c in range(nchunk):
         j0, j1 = c * chunk, min(nk, (c + 1) * chunk)
         s = scale * (q @ k[j0:j1].T)
-        m[:, c] = s.max(axis=1)
-        p = np.exp(s - m[:, c:c + 1])
+        if causal:
+            s = np.where(np.arange(j0, j1)[None, :] <= q_pos[:, None], s, NEG_INF)
+        mc = s.max(axis=1)
+        nonempty = np.isfinite(mc)
+        p = np.exp(s - np.where(nonempty, mc, 0.0)[:, None])   # exp(-inf) = 0
+        m[:, c] = mc
         l[:, c] = p.sum(axis=1)
         acc[:, c, :] = p @ v[j0:j1]
     return m, l, acc

@@ -90,7 +90,37 @@ def _dense_checks(d):
         lse_ref = torch.logsumexp(0.5 * qt @ kt.T, dim=-1).numpy()
         return np.allclose(o, o_ref, rtol=1e-12, atol=1e-12) and np.allclose(lse, lse_ref, rtol=1e-12)
 
-    for name, fn in (("golden", golden), ("sdpa", sdpa), ("gqa", gqa), ("split", split)):
+    def cache():
+        # bottom-right causal alignment with grouped KV heads and Nq < Nk,
+        # against torch SDPA with an explicit mask j <= i + (Nk - Nq)
+        rng = np.random.default_rng(5)
+        q = rng.standard_normal((1, 4, 5, 3))
+        k = rng.standard_normal((1, 2, 9, 3))
+        v = rng.standard_normal((1, 2, 9, 3))
+        o, lse = d.attention_cache(q, k, v, 0.5, True)
+        mask = torch.arange(9)[None, :] <= (torch.arange(5) + 4)[:, None]
+        kt = torch.from_numpy(k).repeat_interleave(2, dim=1)
+        vt = torch.from_numpy(v).repeat_interleave(2, dim=1)
+        o_ref = F.scaled_dot_product_attention(torch.from_numpy(q), kt, vt, attn_mask=mask, scale=0.5).numpy()
+        return np.allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+
+    def causal_split():
+        # merged causal partials, with rows and chunks that hold no eligible
+        # key (Nq > Nk), against the explicit-mask library result
+        rng = np.random.default_rng(6)
+        q = rng.standard_normal((9, 4))
+        k = rng.standard_normal((7, 4))
+        v = rng.standard_normal((7, 4))
+        o, lse = d.merge_partials(*d.split_partials(q, k, v, 0.5, 3, causal=True))
+        if not (np.all(o[:2] == 0.0) and np.all(lse[:2] == -np.inf)) or np.isnan(o).any():
+            return False
+        mask = torch.arange(7)[None, :] <= (torch.arange(9) - 2)[:, None]
+        qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+        o_ref = F.scaled_dot_product_attention(qt[2:], kt, vt, attn_mask=mask[2:], scale=0.5).numpy()
+        return np.allclose(o[2:], o_ref, rtol=1e-12, atol=1e-12)
+
+    for name, fn in (("golden", golden), ("sdpa", sdpa), ("gqa", gqa), ("split", split), ("cache", cache),
+                     ("causal_split", causal_split)):
         try:
             ok = bool(fn())
         except Exception:
@@ -110,7 +140,13 @@ DENSE_MUTANTS = [
     ("merge denominator unrescaled", "big_l = (w * l).sum(axis=-1)", "big_l = l.sum(axis=-1)"),
     ("merge averages outputs", "o = num / np.where(nonempty, big_l, 1.0)[..., None]",
      "o = (acc / np.where(l > 0, l, 1.0)[..., None]).mean(axis=-2)"),
-    ("partial unshifted", "p = np.exp(s - m[:, c:c + 1])", "p = np.exp(s)"),
+    ("partial unshifted", "p = np.exp(s - np.where(nonempty, mc, 0.0)[:, None])", "p = np.exp(s)"),
+    ("empty partial shifted by -inf", "p = np.exp(s - np.where(nonempty, mc, 0.0)[:, None])",
+     "p = np.exp(s - mc[:, None])"),
+    ("causal partial excludes position", "<= q_pos[:, None], s, NEG_INF)", "< q_pos[:, None], s, NEG_INF)"),
+    ("top-left alignment", "return np.arange(nq, dtype=np.int64) + (nk - nq)", "return np.arange(nq, dtype=np.int64)"),
+    ("alignment off by one", "return np.arange(nq, dtype=np.int64) + (nk - nq)",
+     "return np.arange(nq, dtype=np.int64) + (nk - nq - 1)"),
     ("partial numerator without weights", "acc[:, c, :] = p @ v[j0:j1]", "acc[:, c, :] = v[j0:j1].sum(axis=0)"),
 ]
 

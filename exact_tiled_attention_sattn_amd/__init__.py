@@ -15,7 +15,8 @@ import os
 import torch
 
 __all__ = [
-    "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen",
+    "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen", "sattn_fwd_cache",
+    "sattn_fwd_split_cache",
     "SattnError", "library", "LIB_PATH", "STATUS",
 ]
 
@@ -63,6 +64,12 @@ def library():
     lib.sattn_fwd_varlen.restype = i32
     lib.sattn_fwd_varlen.argtypes = [i32, vp, vp, vp, vp, fp, vp, i64, i64, i64, i64, i64, i64, i32,
                                      ctypes.c_float, vp]
+    lib.sattn_fwd_cache.restype = i32
+    lib.sattn_fwd_cache.argtypes = [i32, vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64, i32,
+                                    ctypes.c_float, vp]
+    lib.sattn_fwd_split_cache.restype = i32
+    lib.sattn_fwd_split_cache.argtypes = [i32, vp, vp, vp, fp, fp, fp, i64, i64, i64, i64, i64, i64, i64,
+                                          i32, ctypes.c_float, vp]
     _lib = lib
     return lib
 
@@ -135,22 +142,55 @@ def split_num_chunks(nk, chunk):
     return -(-nk // chunk)
 
 
-def sattn_fwd_split(q, k, v, chunk, scale=None, part_m=None, part_l=None, part_acc=None):
-    """Split-KV partial states (non-causal). q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D].
-
-    Returns (part_m [B,Hq,Nq,C], part_l [B,Hq,Nq,C], part_acc [B,Hq,Nq,C,D]),
-    all float32, acc not normalized."""
-    lib = library()
+def _cache_shapes(q, k, v):
     _dev_tensor(q, "q", ndim=4)
     if q.dtype not in _DTYPE_CODE:
         raise ValueError("q must be float16 or bfloat16")
     _dev_tensor(k, "k", q.dtype, 4)
     _dev_tensor(v, "v", q.dtype, 4)
-    dev = _same_device(q, k, v, part_m, part_l, part_acc)
     b, hq, nq, d = q.shape
     if k.shape != v.shape or k.shape[0] != b or k.shape[3] != d:
         raise ValueError("k/v must be [B, Hkv, Nk, D] matching q")
-    hkv, nk = k.shape[1], k.shape[2]
+    return b, hq, nq, d, k.shape[1], k.shape[2]
+
+
+def sattn_fwd_cache(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Queries [B,Hq,Nq,D] against a K/V cache [B,Hkv,Nk,D]; query i sits at
+    position i + Nk - Nq (causal: keys j <= i + Nk - Nq).
+
+    Returns (o [B,Hq,Nq,D] in q's dtype, lse [B,Hq,Nq] float32)."""
+    lib = library()
+    b, hq, nq, d, hkv, nk = _cache_shapes(q, k, v)
+    dev = _same_device(q, k, v, out, lse)
+    out = torch.empty_like(q) if out is None else _dev_tensor(out, "out", q.dtype, 4)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=dev) if lse is None else \
+        _dev_tensor(lse, "lse", torch.float32, 3)
+    if out.shape != q.shape or lse.shape != (b, hq, nq):
+        raise ValueError("out/lse shape mismatch")
+    with torch.cuda.device(dev):
+        _check(lib.sattn_fwd_cache(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                   b, hq, hkv, nq, nk, d, int(bool(causal)), _scale(scale, d), _stream(dev)))
+    return out, lse
+
+
+def sattn_fwd_split_cache(q, k, v, chunk, causal=False, scale=None, part_m=None, part_l=None, part_acc=None):
+    """Split-KV partial states against a K/V cache, optionally causal (query i
+    at position i + Nk - Nq). Same outputs as ``sattn_fwd_split``."""
+    return _split(q, k, v, chunk, causal, scale, part_m, part_l, part_acc)
+
+
+def sattn_fwd_split(q, k, v, chunk, scale=None, part_m=None, part_l=None, part_acc=None):
+    """Split-KV partial states (non-causal). q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D].
+
+    Returns (part_m [B,Hq,Nq,C], part_l [B,Hq,Nq,C], part_acc [B,Hq,Nq,C,D]),
+    all float32, acc not normalized."""
+    return _split(q, k, v, chunk, None, scale, part_m, part_l, part_acc)
+
+
+def _split(q, k, v, chunk, causal, scale, part_m, part_l, part_acc):
+    lib = library()
+    b, hq, nq, d, hkv, nk = _cache_shapes(q, k, v)
+    dev = _same_device(q, k, v, part_m, part_l, part_acc)
     chunk = int(chunk)
     if chunk <= 0:
         raise ValueError("chunk must be > 0")
@@ -164,9 +204,14 @@ def sattn_fwd_split(q, k, v, chunk, scale=None, part_m=None, part_l=None, part_a
     if part_m.shape != shp or part_l.shape != shp or part_acc.shape != shp + (d,):
         raise ValueError("partial buffer shape mismatch")
     with torch.cuda.device(dev):
-        _check(lib.sattn_fwd_split(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(part_m), _ptr(part_l),
-                                   _ptr(part_acc), b, hq, hkv, nq, nk, d, chunk, _scale(scale, d),
-                                   _stream(dev)))
+        if causal is None:
+            _check(lib.sattn_fwd_split(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(part_m),
+                                       _ptr(part_l), _ptr(part_acc), b, hq, hkv, nq, nk, d, chunk,
+                                       _scale(scale, d), _stream(dev)))
+        else:
+            _check(lib.sattn_fwd_split_cache(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(part_m),
+                                             _ptr(part_l), _ptr(part_acc), b, hq, hkv, nq, nk, d, chunk,
+                                             int(bool(causal)), _scale(scale, d), _stream(dev)))
     return part_m, part_l, part_acc
 
 

@@ -29,7 +29,12 @@
 
 namespace sattn {
 
-enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2 };
+// DENSE: [B, H, N, D] self-attention, equal query/key lengths.
+// VARLEN: packed sequences, grouped KV heads.
+// SPLIT: per-chunk partial states over a key range (optionally causal).
+// CACHE: [B, Hq, Nq, D] queries against a [B, Hkv, Nk, D] key/value cache;
+//        query i sits at logical position i + (Nk - Nq).
+enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_CACHE = 3 };
 
 struct FwdParams {
   const uint16_t* q;
@@ -41,10 +46,11 @@ struct FwdParams {
   float* part_l;
   float* part_acc;
   const int32_t* cu_seqlens;
-  int heads;       // dense: B*H; split: B*Hq
-  int hq, hkv;     // query heads, KV heads (varlen, split)
-  int n;           // dense: N; split: Nq
-  int nk;          // split: Nk
+  int heads;       // dense: B*H; split, cache: B*Hq
+  int hq, hkv;     // query heads, KV heads (varlen, split, cache)
+  int n;           // dense: N; split, cache: Nq
+  int nk;          // split, cache: Nk
+  int off;         // split, cache: Nk - Nq, the logical position of query 0
   int chunk;       // split: keys per chunk
   int nchunks;     // split: C
   int nqt;         // query tiles per slice (dense/split) or per longest sequence (varlen)
@@ -147,6 +153,35 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.k_begin = 0;
     w.k_end = CAUSAL ? min(len, w.q_pos0 + BM) : len;
     return true;
+  } else if constexpr (MODE == MODE_CACHE) {
+    // Logical order: (batch, KV head), then query tile (heaviest first), then
+    // the query heads sharing that KV head, so that the workgroups reading
+    // one cache slice run together on one XCD and its L2.
+    if (item > 0) return false;
+    const int grp = p.hq / p.hkv;
+    const int lin = xcd_linear(bid);
+    const int per_kv = p.nqt * grp;
+    const int kvs = lin / per_kv;                 // b * Hkv + g
+    const int r = lin % per_kv;
+    const int qt = p.nqt - 1 - r / grp;
+    const int h = (kvs % p.hkv) * grp + r % grp;
+    const int b = kvs / p.hkv;
+    const int row0 = qt * BM;
+    const int64_t qslice = ((int64_t)b * p.hq + h) * p.n;
+    w.nq = min(BM, p.n - row0);
+    w.q_pos0 = row0 + p.off;
+    w.q = p.q + (qslice + row0) * D;
+    w.o = p.o + (qslice + row0) * D;
+    w.lse = p.lse + qslice + row0;
+    w.k = p.k + (int64_t)kvs * p.nk * D;
+    w.v = p.v + (int64_t)kvs * p.nk * D;
+    w.q_rs = D;
+    w.kv_rs = D;
+    w.k_begin = 0;
+    // causal: keys after the tile's last query are never eligible; a tile
+    // whose queries all precede the cache has no key at all
+    w.k_end = CAUSAL ? min(p.nk, max(0, w.q_pos0 + BM)) : p.nk;
+    return w.nq > 0;
   } else {
     // Split-KV: block id -> (slice, query tile, chunk), chunk fastest.
     const int c = bid % p.nchunks;
@@ -156,9 +191,10 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     const int b = slice / p.hq;
     const int h = slice % p.hq;
     const int g = h / (p.hq / p.hkv);
-    w.q_pos0 = qt * BM;
-    w.nq = min(BM, p.n - w.q_pos0);
-    w.q = p.q + ((int64_t)slice * p.n + w.q_pos0) * D;
+    const int row0 = qt * BM;
+    w.nq = min(BM, p.n - row0);
+    w.q_pos0 = row0 + p.off;
+    w.q = p.q + ((int64_t)slice * p.n + row0) * D;
     w.o = nullptr;
     w.lse = nullptr;
     const int64_t kvbase = ((int64_t)b * p.hkv + g) * p.nk * D;
@@ -168,8 +204,11 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.kv_rs = D;
     w.k_begin = c * p.chunk;
     w.k_end = min(p.nk, w.k_begin + p.chunk);
-    w.part_row0 = ((int64_t)slice * p.n + w.q_pos0) * p.nchunks + c;
-    return w.nq > 0 && w.k_begin < w.k_end;
+    // causal: keys after the tile's last query are never eligible; a chunk
+    // with none left still writes its rows' empty states
+    if (CAUSAL) w.k_end = max(w.k_begin, min(w.k_end, w.q_pos0 + BM));
+    w.part_row0 = ((int64_t)slice * p.n + row0) * p.nchunks + c;
+    return w.nq > 0;
   }
 }
 
@@ -232,6 +271,10 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   constexpr int KB = BN / 32;              // 32-key blocks per tile
   constexpr int DB = D / 32;               // 32-wide d blocks of the output
   constexpr bool LAZY = (MODE != MODE_SPLIT);
+  // Rows that can have no eligible key in the keys walked here: queries
+  // before the cache or an empty cache, or a causal chunk after a query. Their max stays -inf,
+  // and exps are then taken against 0 so that masked scores give 0, not NaN.
+  constexpr bool EMPTY_ROWS = MODE == MODE_CACHE || (CAUSAL && MODE == MODE_SPLIT);
   constexpr float LAZY_TH = 8.0f;
   static_assert(NI >= 1 && TILE_BYTES % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
@@ -374,12 +417,13 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
 
     if constexpr (FAST) {
       // ---- fixed-reference update: exps against the row's first-tile max
+      const float mref = (EMPTY_ROWS && m == -INFINITY) ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[kb][r], c, -m));
+          const float pv = fast_exp2(fmaf(s[kb][r], c, -mref));
           s[kb][r] = pv;
           rs += pv;
         }
@@ -407,12 +451,13 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       }
+      const float mref = (EMPTY_ROWS && m == -INFINITY) ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[kb][r], c, -m));
+          const float pv = fast_exp2(fmaf(s[kb][r], c, -mref));
           s[kb][r] = pv;
           rs += pv;
         }
@@ -479,7 +524,8 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
 
   if constexpr (MODE != MODE_SPLIT) {
     if (!row_ok) return;
-    const float inv = 1.f / lt;
+    // an empty row (no eligible key) gives O = 0 and lse = -inf
+    const float inv = (EMPTY_ROWS && lt == 0.f) ? 0.f : 1.f / lt;
     uint16_t* op = w.o + (int64_t)qrow * w.q_rs;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

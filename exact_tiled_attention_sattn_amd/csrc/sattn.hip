@@ -133,16 +133,18 @@ void dispatch_fwd(int dtype, int64_t D, bool causal, const FwdParams& p, int64_t
 #undef SATTN_CASE
 }
 
-// The split path is non-causal only.
+// Split-KV partial states over key chunks; causal chunks use the
+// bottom-right alignment (query i at position i + Nk - Nq).
+template <bool CAUSAL>
 void dispatch_split(int dtype, int64_t D, const FwdParams& p, int64_t grid, hipStream_t s) {
   if (dtype == SATTN_BF16) {
-    if (D == 32) launch_fwd<Bf16, 32, false, MODE_SPLIT>(p, grid, s);
-    else if (D == 64) launch_fwd<Bf16, 64, false, MODE_SPLIT>(p, grid, s);
-    else launch_fwd<Bf16, 128, false, MODE_SPLIT>(p, grid, s);
+    if (D == 32) launch_fwd<Bf16, 32, CAUSAL, MODE_SPLIT>(p, grid, s);
+    else if (D == 64) launch_fwd<Bf16, 64, CAUSAL, MODE_SPLIT>(p, grid, s);
+    else launch_fwd<Bf16, 128, CAUSAL, MODE_SPLIT>(p, grid, s);
   } else {
-    if (D == 32) launch_fwd<F16, 32, false, MODE_SPLIT>(p, grid, s);
-    else if (D == 64) launch_fwd<F16, 64, false, MODE_SPLIT>(p, grid, s);
-    else launch_fwd<F16, 128, false, MODE_SPLIT>(p, grid, s);
+    if (D == 32) launch_fwd<F16, 32, CAUSAL, MODE_SPLIT>(p, grid, s);
+    else if (D == 64) launch_fwd<F16, 64, CAUSAL, MODE_SPLIT>(p, grid, s);
+    else launch_fwd<F16, 128, CAUSAL, MODE_SPLIT>(p, grid, s);
   }
 }
 
@@ -247,9 +249,9 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
   return launch_status();
 }
 
-int sattn_fwd_split(int dtype, const void* q, const void* k, const void* v, float* part_m, float* part_l,
-                    float* part_acc, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
-                    int64_t chunk, float scale, void* stream) {
+static int split_impl(int dtype, const void* q, const void* k, const void* v, float* part_m, float* part_l,
+                      float* part_acc, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                      int64_t chunk, bool causal, float scale, void* stream) {
   int st = check_common(dtype, D, scale);
   if (st) return st;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return fail(SATTN_ERR_SHAPE, "negative size");
@@ -295,7 +297,63 @@ int sattn_fwd_split(int dtype, const void* q, const void* k, const void* v, floa
   p.chunk = (int)(chunk < Nk ? chunk : Nk);  // chunk >= Nk: one chunk holds every key
   p.nchunks = (int)C;
   p.nqt = (int)nqt;
-  dispatch_split(dtype, D, p, grid, (hipStream_t)stream);
+  p.off = (int)(Nk - Nq);
+  if (causal) dispatch_split<true>(dtype, D, p, grid, (hipStream_t)stream);
+  else dispatch_split<false>(dtype, D, p, grid, (hipStream_t)stream);
+  return launch_status();
+}
+
+int sattn_fwd_split(int dtype, const void* q, const void* k, const void* v, float* part_m, float* part_l,
+                    float* part_acc, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                    int64_t chunk, float scale, void* stream) {
+  return split_impl(dtype, q, k, v, part_m, part_l, part_acc, B, Hq, Hkv, Nq, Nk, D, chunk, false, scale, stream);
+}
+
+int sattn_fwd_split_cache(int dtype, const void* q, const void* k, const void* v, float* part_m, float* part_l,
+                          float* part_acc, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                          int64_t chunk, int causal, float scale, void* stream) {
+  return split_impl(dtype, q, k, v, part_m, part_l, part_acc, B, Hq, Hkv, Nq, Nk, D, chunk, causal != 0, scale,
+                    stream);
+}
+
+int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                    int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
+                    void* stream) {
+  int st = check_common(dtype, D, scale);
+  if (st) return st;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return fail(SATTN_ERR_SHAPE, "Hq must be a multiple of Hkv");
+  int64_t qrows, kvrows, qbytes, kvbytes;
+  if (!product({B, Hq, Nq}, &qrows) || !product({B, Hkv, Nk}, &kvrows) || !product({qrows, D, 2}, &qbytes) ||
+      !product({kvrows, D, 2}, &kvbytes))
+    return fail(SATTN_ERR_SHAPE, "size overflow");
+  if (qrows == 0) return ok();
+  if (Nq >= kMaxLen || Nk >= kMaxLen || B * Hq >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "size too large");
+  if (Nk * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
+  if (!q || !o || !lse || (kvbytes > 0 && (!k || !v))) return fail(SATTN_ERR_NULL, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return fail(SATTN_ERR_ALIGN, "q/k/v/o need 16-byte and lse 4-byte alignment");
+  Range ins[3] = {range_of(q, qbytes, "q"), range_of(k, kvbytes, "k"), range_of(v, kvbytes, "v")};
+  Range outs[2] = {range_of(o, qbytes, "o"), range_of(lse, qrows * 4, "lse")};
+  if ((st = check_alias(ins, 3, outs, 2))) return st;
+  const int bm = tile_m<MODE_CACHE>(D);
+  const int64_t nqt = (Nq + bm - 1) / bm;
+  const int64_t grid = B * Hq * nqt;
+  if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
+  FwdParams p = blank_params(scale);
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (uint16_t*)o;
+  p.lse = lse;
+  p.heads = (int)(B * Hq);
+  p.hq = (int)Hq;
+  p.hkv = (int)Hkv;
+  p.n = (int)Nq;
+  p.nk = (int)Nk;
+  p.off = (int)(Nk - Nq);
+  p.nqt = (int)nqt;
+  dispatch_fwd<MODE_CACHE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
   return launch_status();
 }
 

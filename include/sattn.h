@@ -104,8 +104,8 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
  *                NOT divided by l.
  * The three buffers are private to this call and its following
  * sattn_merge (enqueue the merge on the same stream, or after an event).
- * Nk must be > 0 when B*Hq*Nq > 0. Causal split is not implemented
- * (there is no causal argument).
+ * Nk must be > 0 when B*Hq*Nq > 0. This entry point is non-causal; the
+ * causal split over a key/value cache is sattn_fwd_split_cache.
  */
 int sattn_fwd_split(int dtype, const void* q, const void* k, const void* v,
                     float* part_m, float* part_l, float* part_acc,
@@ -146,6 +146,44 @@ int sattn_merge(int dtype, const float* part_m, const float* part_l, const float
 int sattn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                      const int32_t* cu_seqlens, int64_t S, int64_t T, int64_t max_seqlen,
                      int64_t Hq, int64_t Hkv, int64_t D, int causal, float scale, void* stream);
+
+/*
+ * Queries against a key/value cache of another length, with grouped KV
+ * heads ("Attention algorithms and data movement", lesson 04: unequal-length
+ * alignment and empty rows from logical positions; lesson 05: GQA head
+ * mapping and the cache payload shared by a group of query heads).
+ *
+ *   q, o       : [B, Hq, Nq, D];  k, v : [B, Hkv, Nk, D]  (dtype `dtype`).
+ *   lse        : [B, Hq, Nq] float32.
+ *   Query head h reads KV head h / (Hq / Hkv); Hq % Hkv must be 0.
+ *   The queries are the last Nq tokens of a sequence whose cache holds Nk
+ *   positions: query i sits at logical position i + (Nk - Nq)
+ *   (bottom-right alignment; Nq = Nk is ordinary self-attention, Nq = 1 a
+ *   decode step, 1 < Nq < Nk a chunk of a chunked prefill).
+ *   causal     : nonzero -> key j is eligible for query i iff
+ *                j <= i + (Nk - Nq); zero -> all Nk keys are eligible.
+ *   A query with no eligible key (i + Nk - Nq < 0 when Nq > Nk, or Nk = 0)
+ *   is an empty row: O = 0 and lse = -inf. k and v may be NULL when Nk = 0.
+ * Key tiles after a query tile's last position are skipped, not masked.
+ */
+int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                    int causal, float scale, void* stream);
+
+/*
+ * Split-KV partial states against a key/value cache, optionally causal:
+ * sattn_fwd_split with the alignment of sattn_fwd_cache (query i at logical
+ * position i + (Nk - Nq)). Same shapes, buffers and merge as sattn_fwd_split;
+ * with causal nonzero only keys j <= i + (Nk - Nq) of each chunk count, and a
+ * chunk holding no eligible key for a row stores that row's empty state
+ * (part_m = -inf, part_l = 0, part_acc = 0), the identity of sattn_merge
+ * ("Attention algorithms and data movement", lesson 01).
+ * causal = 0 gives exactly sattn_fwd_split.
+ */
+int sattn_fwd_split_cache(int dtype, const void* q, const void* k, const void* v,
+                          float* part_m, float* part_l, float* part_acc,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                          int64_t chunk, int causal, float scale, void* stream);
 
 #ifdef __cplusplus
 }

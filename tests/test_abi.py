@@ -30,8 +30,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen",
-              "sattn_status_string", "sattn_last_error"):
+    for n in ("sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen", "sattn_fwd_cache",
+              "sattn_fwd_split_cache", "sattn_status_string", "sattn_last_error"):
         assert n in names
 
 
@@ -154,3 +154,50 @@ def test_binding_checks_cu_seqlens_on_host():
     for bad, t, mx in (([1, 3], 3, 5), ([0, 5, 4], 4, 5), ([0, 4], 5, 5), ([0, 9], 9, 8)):
         with pytest.raises(ValueError):
             check_cu_seqlens(bad, t, mx)
+
+
+def _cache(lib, b=1, hq=4, hkv=2, nq=8, nk=100, d=128, causal=1, q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5,
+           scale=0.1):
+    return lib.sattn_fwd_cache(1, q, k, v, o, lse, b, hq, hkv, nq, nk, d, causal, F32(scale), NULL)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(hq=6, hkv=4), "SATTN_ERR_SHAPE"),
+    (dict(hkv=0), "SATTN_ERR_SHAPE"),
+    (dict(nk=-1), "SATTN_ERR_SHAPE"),
+    (dict(nq=-1), "SATTN_ERR_SHAPE"),
+    (dict(d=80), "SATTN_ERR_UNSUPPORTED"),
+    (dict(nk=1 << 31), "SATTN_ERR_UNSUPPORTED"),
+    (dict(scale=0.0), "SATTN_ERR_VALUE"),
+    (dict(k=NULL), "SATTN_ERR_NULL"),
+    (dict(lse=NULL), "SATTN_ERR_NULL"),
+    (dict(o=ctypes.c_void_p(0x40008)), "SATTN_ERR_ALIGN"),
+    (dict(o=FAKE2), "SATTN_ERR_ALIAS"),                             # o == k
+    (dict(lse=ctypes.c_void_p(0x40000 + 64)), "SATTN_ERR_ALIAS"),   # lse inside o
+])
+def test_cache_rejects(lib, kwargs, status):
+    st = _cache(lib, **kwargs)
+    assert STATUS[st] == status, (STATUS[st], lib.sattn_last_error())
+
+
+def test_cache_zero_queries_ok_without_pointers(lib):
+    assert _cache(lib, nq=0, q=NULL, k=NULL, v=NULL, o=NULL, lse=NULL) == 0
+    assert _cache(lib, hq=0, q=NULL, k=NULL, v=NULL, o=NULL, lse=NULL) == 0
+
+
+def test_split_cache_rejects(lib):
+    pm, pl, pa = ctypes.c_void_p(0x900000), ctypes.c_void_p(0xA00000), ctypes.c_void_p(0xB00000)
+
+    def call(**kw):
+        a = dict(b=1, hq=4, hkv=2, nq=3, nk=100, d=128, chunk=32, causal=1, pm=pm)
+        a.update(kw)
+        return STATUS[lib.sattn_fwd_split_cache(1, FAKE, FAKE2, FAKE3, a["pm"], pl, pa, a["b"], a["hq"], a["hkv"],
+                                                a["nq"], a["nk"], a["d"], a["chunk"], a["causal"], F32(0.1),
+                                                NULL)]
+    assert call(chunk=0) == "SATTN_ERR_SHAPE"
+    assert call(hq=3) == "SATTN_ERR_SHAPE"
+    assert call(nk=0) == "SATTN_ERR_SHAPE"
+    assert call(d=16) == "SATTN_ERR_UNSUPPORTED"
+    assert call(pm=FAKE) == "SATTN_ERR_ALIAS"
+    assert call(pm=NULL) == "SATTN_ERR_NULL"
+    assert call(nq=0, pm=NULL) == "SATTN_OK"

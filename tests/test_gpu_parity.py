@@ -13,7 +13,7 @@ import torch
 
 import workloads as W
 from exact_tiled_attention_sattn_amd import (sattn_fwd, sattn_fwd_split, sattn_merge, sattn_fwd_varlen,
-                                             SattnError)
+                                             sattn_fwd_cache, sattn_fwd_split_cache, SattnError)
 from oracle import dense
 from tests.parity import check_attention, check_o, check_lse, TOL
 
@@ -428,3 +428,136 @@ def test_score_growth_varlen_fallback():
     torch.cuda.synchronize()
     o_ref, lse_ref = dense.varlen_gqa(W.to_f64(q), W.to_f64(k), W.to_f64(v), cu, W.scale_f32(128), True)
     check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "growth varlen")
+
+
+# ------------------------------------------------- queries against a K/V cache
+CACHE_SMALL = [
+    # (B, Hq, Hkv, Nq, Nk, D, dtype)
+    (1, 2, 1, 1, 300, 128, "bf16"),      # one decode query
+    (1, 4, 2, 37, 300, 64, "fp16"),      # a prefill chunk, ragged tiles
+    (2, 4, 4, 129, 129, 32, "bf16"),     # equal lengths
+    (1, 2, 1, 200, 70, 128, "bf16"),     # more queries than cache: empty rows
+    (1, 8, 2, 300, 1000, 128, "fp16"),   # several tiles both ways, 4 heads per KV head
+    (1, 2, 2, 5, 0, 64, "bf16"),         # empty cache
+]
+
+
+def _cache_run(b, hq, hkv, nq, nk, d, dt, causal, seed):
+    q, k, v = W.qkv((b, hq, nq, d), (b, hkv, nk, d), dt, seed)
+    scale = W.scale_f32(d)
+    o, lse = sattn_fwd_cache(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return q, k, v, scale, o, lse
+
+
+@pytest.mark.parametrize("b,hq,hkv,nq,nk,d,dt", CACHE_SMALL)
+@pytest.mark.parametrize("causal", [False, True])
+def test_cache_small_full(b, hq, hkv, nq, nk, d, dt, causal):
+    _banner("cache", b, hq, hkv, nq, nk, d, dt, causal)
+    q, k, v, scale, o, lse = _cache_run(b, hq, hkv, nq, nk, d, dt, causal, seed=5000 + nq + nk)
+    o_ref, lse_ref = dense.attention_cache(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "cache")
+
+
+def test_cache_empty_rows_exact():
+    """Queries before the cache: O is exactly 0 and lse exactly -inf."""
+    _banner("cache empty rows")
+    _, _, _, _, o, lse = _cache_run(1, 2, 1, 300, 44, 128, "bf16", True, seed=5101)
+    assert torch.count_nonzero(o[:, :, :256].float()).item() == 0
+    assert bool((lse[:, :, :256] == -float("inf")).all())
+    assert torch.isfinite(lse[:, :, 256:]).all()
+
+
+def test_cache_equal_lengths_matches_fwd_bitwise():
+    """Nq = Nk with one KV head per query head gives each row the same
+    arithmetic as sattn_fwd (same 64-key tiles in the same order; the
+    workgroups differ in size only): bitwise equal."""
+    _banner("cache == fwd")
+    q, k, v = (x.to(DEV) for x in _dense_inputs(1, 3, 700, 128, "bf16", seed=5102))
+    for causal in (False, True):
+        o1, l1 = sattn_fwd(q, k, v, causal=causal)
+        o2, l2 = sattn_fwd_cache(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), causal
+
+
+def test_cache_future_perturbation_bitwise():
+    """Changing cache position j leaves every query at a position before j
+    bitwise unchanged (bottom-right alignment)."""
+    _banner("cache future perturbation")
+    nq, nk = 200, 500
+    q, k, v = W.qkv((1, 4, nq, 128), (1, 2, nk, 128), "bf16", 5103)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    o0, l0 = sattn_fwd_cache(q, k, v, causal=True)
+    for j in (300, 301, 364, 499):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, :, j] = 30.0
+        v2[:, :, j] = -500.0
+        o1, l1 = sattn_fwd_cache(q, k2, v2, causal=True)
+        i = j - (nk - nq)          # first query whose position is >= j
+        assert torch.equal(o1[:, :, :i], o0[:, :, :i]) and torch.equal(l1[:, :, :i], l0[:, :, :i]), j
+        assert not torch.equal(o1[:, :, i:], o0[:, :, i:])
+
+
+def test_cache_chunked_prefill_sampled():
+    """A 2048-token chunk against a 16384-token cache, 32 query heads on 8
+    KV heads, bf16 causal: sampled rows per head, edges included."""
+    _banner("chunked prefill 2048 vs 16384")
+    b, hq, hkv, nq, nk, d = 1, 32, 8, 2048, 16384, 128
+    q, k, v, scale, o, lse = _cache_run(b, hq, hkv, nq, nk, d, "bf16", True, seed=5104)
+    rows = W.sample_rows(5104, nq, 16, groups=b * hq).reshape(b, hq, -1)
+    o_ref, lse_ref = dense.attention_cache(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, True, rows=rows)
+    idx = torch.from_numpy(rows)
+    oc, lc = o.cpu(), lse.cpu()
+    o_s = torch.stack([torch.stack([oc[0, h][idx[0, h]] for h in range(hq)])])
+    l_s = torch.stack([torch.stack([lc[0, h][idx[0, h]] for h in range(hq)])])
+    check_attention(o_s, l_s, o_ref, lse_ref, torch.bfloat16, "chunked prefill")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+SPLIT_CACHE_SMALL = [
+    # (B, Hq, Hkv, Nq, Nk, D, chunk, dtype)
+    (1, 4, 1, 1, 1000, 128, 256, "bf16"),    # causal decode: equals non-causal
+    (1, 2, 2, 16, 700, 128, 128, "bf16"),    # a few queries: last chunk partly eligible
+    (1, 2, 1, 300, 260, 64, 64, "fp16"),     # more queries than keys: empty rows
+    (2, 2, 1, 70, 70, 32, 16, "fp16"),       # equal lengths, many empty chunks
+]
+
+
+@pytest.mark.parametrize("b,hq,hkv,nq,nk,d,chunk,dt", SPLIT_CACHE_SMALL)
+def test_split_cache_causal_partials_and_merge(b, hq, hkv, nq, nk, d, chunk, dt):
+    _banner("split cache causal", b, hq, hkv, nq, nk, d, chunk, dt)
+    q, k, v = W.qkv((b, hq, nq, d), (b, hkv, nk, d), dt, seed=6000 + nq + nk)
+    scale = W.scale_f32(d)
+    pm, pl, pa = sattn_fwd_split_cache(q.to(DEV), k.to(DEV), v.to(DEV), chunk, causal=True, scale=scale)
+    o, lse = sattn_merge(pm, pl, pa, W.DTYPES[dt])
+    torch.cuda.synchronize()
+    qf, kf, vf = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    g = hq // hkv
+    pm_, pl_, pa_ = (x.cpu().double().numpy() for x in (pm, pl, pa))
+    o_ref, lse_ref = dense.attention_cache(qf, kf, vf, scale, True)
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "merged")
+    for bb in range(b):
+        for h in range(hq):
+            m_ref, l_ref, a_ref = dense.split_partials(qf[bb, h], kf[bb, h // g], vf[bb, h // g], scale, chunk,
+                                                       causal=True)
+            empty = np.isinf(m_ref)
+            # empty states exactly; the others by their max, logsumexp and output
+            assert np.all(pm_[bb, h][empty] == -np.inf) and np.all(pl_[bb, h][empty] == 0.0)
+            assert np.all(pa_[bb, h][empty] == 0.0)
+            np.testing.assert_allclose(pm_[bb, h][~empty], m_ref[~empty], rtol=0, atol=1e-3)
+            ok = ~empty
+            check_lse(pm_[bb, h][ok] + np.log(pl_[bb, h][ok]), m_ref[ok] + np.log(l_ref[ok]), "partial lse")
+            check_o(pa_[bb, h][ok] / pl_[bb, h][ok][..., None], a_ref[ok] / l_ref[ok][..., None],
+                    W.DTYPES[dt], "partial o")
+
+
+def test_split_cache_noncausal_is_split_bitwise():
+    _banner("split cache noncausal == split")
+    q, k, v = W.qkv((1, 4, 3, 128), (1, 2, 900, 128), "bf16", 6100)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    a = sattn_fwd_split(q, k, v, 256)
+    b_ = sattn_fwd_split_cache(q, k, v, 256, causal=False)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b_):
+        assert torch.equal(x, y)

@@ -51,6 +51,7 @@ struct FwdParams {
   int n;           // dense: N; split, cache: Nq
   int nk;          // split, cache: Nk
   int off;         // split, cache: Nk - Nq, the logical position of query 0
+  int pack;        // split: 1 = a slice is (batch, KV head) holding the Hq/Hkv query heads' rows
   int chunk;       // split: keys per chunk
   int nchunks;     // split: C
   int nqt;         // query tiles per slice (dense/split) or per longest sequence (varlen)
@@ -69,7 +70,9 @@ struct Work {
   float* lse;          // lse of row 0 of this query tile (stride 1 per row)
   int64_t q_rs;        // row strides in elements
   int64_t kv_rs;
-  int q_pos0;          // logical position of row 0
+  int q_pos0;          // logical position of row 0 (pos_mod > 0: of every row with (row0 + r) % pos_mod == 0)
+  int pos_mod;         // 0: row r sits at q_pos0 + r; else at q_pos0 + (row0 + r) % pos_mod
+  int row0;            // first row of this tile within its slice (used when pos_mod > 0)
   int nq;              // valid rows in this tile
   int k_begin, k_end;  // keys [k_begin, k_end) of the slice
   int64_t part_row0;   // split: index (slice_row * C + c) of row 0
@@ -118,6 +121,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.lse = p.lse + (int64_t)head * p.n + w.q_pos0;
     w.k_begin = 0;
     w.k_end = CAUSAL ? min(p.n, w.q_pos0 + BM) : p.n;
+    w.pos_mod = 0;
     return w.nq > 0;
   } else if constexpr (MODE == MODE_VARLEN) {
     // Logical order: KV head, then sequence, then query tile (heaviest
@@ -152,6 +156,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.lse = p.lse + (int64_t)h * p.total + a + w.q_pos0;
     w.k_begin = 0;
     w.k_end = CAUSAL ? min(len, w.q_pos0 + BM) : len;
+    w.pos_mod = 0;
     return true;
   } else if constexpr (MODE == MODE_CACHE) {
     // Logical order: (batch, KV head), then query tile (heaviest first), then
@@ -181,33 +186,50 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     // causal: keys after the tile's last query are never eligible; a tile
     // whose queries all precede the cache has no key at all
     w.k_end = CAUSAL ? min(p.nk, max(0, w.q_pos0 + BM)) : p.nk;
+    w.pos_mod = 0;
     return w.nq > 0;
   } else {
-    // Split-KV: block id -> (slice, query tile, chunk), chunk fastest.
+    // Split-KV: block id -> (slice, query tile, chunk), chunk fastest. A
+    // slice is one (batch, query head); packed, it is one (batch, KV head)
+    // whose rows are the Nq queries of each of its Hq/Hkv query heads in
+    // turn (contiguous in [B, Hq, Nq] order), so each K/V chunk is read once
+    // for the whole group ("Attention algorithms and data movement", lesson
+    // 05: the cache payload is shared by the group's query heads).
     const int c = bid % p.nchunks;
     const int rest = bid / p.nchunks;
     const int qt = rest % p.nqt;
-    const int slice = rest / p.nqt;          // b * Hq + h
-    const int b = slice / p.hq;
-    const int h = slice % p.hq;
-    const int g = h / (p.hq / p.hkv);
+    const int slice = rest / p.nqt;
+    const int grp = p.hq / p.hkv;
+    int64_t first_row;                       // row of [B*Hq*Nq] where the slice starts
+    int nrows, kvs;
+    if (p.pack) {                            // slice = b * Hkv + g
+      first_row = ((int64_t)(slice / p.hkv) * p.hq + (int64_t)(slice % p.hkv) * grp) * p.n;
+      nrows = grp * p.n;
+      kvs = slice;
+    } else {                                 // slice = b * Hq + h
+      first_row = (int64_t)slice * p.n;
+      nrows = p.n;
+      kvs = (slice / p.hq) * p.hkv + (slice % p.hq) / grp;
+    }
     const int row0 = qt * BM;
-    w.nq = min(BM, p.n - row0);
-    w.q_pos0 = row0 + p.off;
-    w.q = p.q + ((int64_t)slice * p.n + row0) * D;
+    w.nq = min(BM, nrows - row0);
+    w.row0 = row0;
+    w.pos_mod = p.pack ? p.n : 0;
+    w.q_pos0 = p.pack ? p.off : row0 + p.off;
+    w.q = p.q + (first_row + row0) * D;
     w.o = nullptr;
     w.lse = nullptr;
-    const int64_t kvbase = ((int64_t)b * p.hkv + g) * p.nk * D;
+    const int64_t kvbase = (int64_t)kvs * p.nk * D;
     w.k = p.k + kvbase;
     w.v = p.v + kvbase;
     w.q_rs = D;
     w.kv_rs = D;
     w.k_begin = c * p.chunk;
     w.k_end = min(p.nk, w.k_begin + p.chunk);
-    // causal: keys after the tile's last query are never eligible; a chunk
-    // with none left still writes its rows' empty states
-    if (CAUSAL) w.k_end = max(w.k_begin, min(w.k_end, w.q_pos0 + BM));
-    w.part_row0 = ((int64_t)slice * p.n + row0) * p.nchunks + c;
+    // causal: keys after the tile's last position are never eligible; a
+    // chunk with none left still writes its rows' empty states
+    if (CAUSAL) w.k_end = max(w.k_begin, min(w.k_end, p.pack ? p.off + p.n : w.q_pos0 + BM));
+    w.part_row0 = (first_row + row0) * p.nchunks + c;
     return w.nq > 0;
   }
 }
@@ -305,9 +327,10 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   float m = -INFINITY;  // running (possibly stale) max, log2 units
   float l = 0.f;        // this lane's part of the exp-sum
 
-  const int my_pos = w.q_pos0 + qrow;
-  const int wave_first_pos = w.q_pos0 + wave * 32;
-  const int wave_last_pos = wave_first_pos + 31;
+  // Logical position of this lane's row, and the last position of the wave's
+  // rows (packed split rows repeat the Nq positions once per query head).
+  const int my_pos = w.pos_mod ? w.q_pos0 + (w.row0 + qrow) % w.pos_mod : w.q_pos0 + qrow;
+  const int wave_last_pos = w.pos_mod ? w.q_pos0 + w.pos_mod - 1 : w.q_pos0 + wave * 32 + 31;
   const bool wave_active = wave * 32 < w.nq;
   const float c = p.c;
   const int ntiles = (w.k_end - w.k_begin + BN - 1) / BN;

@@ -279,8 +279,14 @@ static int split_impl(int dtype, const void* q, const void* k, const void* v, fl
   if ((st = check_alias(ins, 3, outs, 3))) return st;
 
   const int bm = tile_m<MODE_SPLIT>(D);
-  const int64_t nqt = (Nq + bm - 1) / bm;
-  const int64_t grid = qrows / Nq * nqt * C;
+  // Few queries per head (decode) with grouped KV heads: one slice per
+  // (batch, KV head) holding the group's rows, so each chunk of the cache is
+  // read once per group instead of once per query head.
+  const bool pack = Hq > Hkv && Nq <= 64;
+  const int64_t slices = pack ? B * Hkv : B * Hq;
+  const int64_t slice_rows = pack ? (Hq / Hkv) * Nq : Nq;
+  const int64_t nqt = (slice_rows + bm - 1) / bm;
+  const int64_t grid = slices * nqt * C;
   if (grid >= (int64_t(1) << 31) || C >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
   FwdParams p = blank_params(scale);
   p.q = (const uint16_t*)q;
@@ -298,6 +304,7 @@ static int split_impl(int dtype, const void* q, const void* k, const void* v, fl
   p.nchunks = (int)C;
   p.nqt = (int)nqt;
   p.off = (int)(Nk - Nq);
+  p.pack = pack ? 1 : 0;
   if (causal) dispatch_split<true>(dtype, D, p, grid, (hipStream_t)stream);
   else dispatch_split<false>(dtype, D, p, grid, (hipStream_t)stream);
   return launch_status();

@@ -195,7 +195,8 @@ def test_alias_rejected_on_device():
 
 # ---------------------------------------------------------------- split
 SPLIT_SMALL = [
-    # (B, Hq, Hkv, Nq, Nk, D, chunk, dtype)
+    # (B, Hq, Hkv, Nq, Nk, D, chunk, dtype); Hq > Hkv with Nq <= 64 packs a
+    # KV head's query heads into one slice
     (1, 2, 2, 1, 100, 128, 32, "bf16"),
     (2, 4, 1, 1, 4096, 128, 1024, "bf16"),
     (1, 4, 2, 3, 777, 64, 256, "fp16"),
@@ -521,6 +522,11 @@ SPLIT_CACHE_SMALL = [
     (1, 2, 2, 16, 700, 128, 128, "bf16"),    # a few queries: last chunk partly eligible
     (1, 2, 1, 300, 260, 64, 64, "fp16"),     # more queries than keys: empty rows
     (2, 2, 1, 70, 70, 32, 16, "fp16"),       # equal lengths, many empty chunks
+    # grouped heads packed into one slice per KV head (Nq <= 64): rows of
+    # several query heads share a tile and repeat the same positions
+    (1, 8, 2, 5, 333, 128, 64, "bf16"),
+    (2, 6, 2, 40, 500, 64, 128, "fp16"),     # 120 rows per slice over two 64-row tiles
+    (1, 4, 1, 64, 64, 32, 32, "bf16"),       # every row's own chunk cut at its position
 ]
 
 

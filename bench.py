@@ -313,6 +313,42 @@ def gqa_decode_extra(steps):
             "algorithmic_bytes_split": split_bytes}
 
 
+def strided_extra(steps):
+    """Transposed inputs: q, k, v stored [B, N, H, D] (B=4, H=16, N=4096,
+    D=128 bf16) and viewed as [B, H, N, D]. Loaded in place by
+    sattn_fwd_strided, against copying them to [B, H, N, D] first and running
+    the same kernel on the copies (the copy inside the timing, as in the
+    pages' strided-input comparison)."""
+    from exact_tiled_attention_sattn_amd import sattn_fwd_strided, sattn_fwd_cache
+    b, h, n, d = 4, 16, 4096, 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    q, k, v = (W.randn_device_sliced((b, n, h, d), "bf16", g, DEV).permute(0, 2, 1, 3) for _ in range(3))
+    scale = W.scale_f32(d)
+    o = torch.empty((b, h, n, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=DEV)
+    res = {"workload": "transposed [B,N,H,D] inputs viewed as [B,H,N,D], 4x16x4096x128 bf16"}
+    for causal in (False, True):
+        direct = lambda: sattn_fwd_strided(q, k, v, causal=causal, scale=scale, out=o, lse=lse)  # noqa: E731
+        direct()
+        torch.cuda.synchronize()
+        r = torch.tensor([0, 2047, n - 1])
+        gate_rows(o[1, 5].cpu(), lse[1, 5].cpu(), q[1, 5], k[1, 5], v[1, 5], scale, causal, r, r, torch.bfloat16,
+                  "gate strided")
+
+        def copied():
+            sattn_fwd_cache(q.contiguous(), k.contiguous(), v.contiguous(), causal=causal, scale=scale, out=o, lse=lse)
+        ms_d = float(np.mean(time_launches(direct, steps, 2)))
+        ms_c = float(np.mean(time_launches(copied, steps, 2)))
+        fl = dense_flops(b, h, n, d, causal)
+        tag = "causal" if causal else "noncausal"
+        res[tag] = {"direct_ms": ms_d, "copy_then_kernel_ms": ms_c, "direct_TFLOPs": fl / ms_d / 1e9,
+                    "copy_then_kernel_TFLOPs": fl / ms_c / 1e9}
+    del q, k, v
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(budget_s):
     """The FP64 oracle on sampled query rows of the batched workload, both
     variants, on the host cores, scaled to TFLOP/s by the sampled fraction."""
@@ -475,6 +511,8 @@ def main():
         extras["cache_prefill"] = prefill_extra(max(3, min(args.steps, 10)))
         log("causal GQA decode against a K/V cache")
         extras["cache_gqa_decode"] = gqa_decode_extra(max(3, min(args.steps, 10)))
+        log("strided (transposed) inputs")
+        extras["strided_transposed"] = strided_extra(max(3, min(args.steps, 10)))
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

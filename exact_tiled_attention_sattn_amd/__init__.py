@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen", "sattn_fwd_cache",
-    "sattn_fwd_split_cache",
+    "sattn_fwd_split_cache", "sattn_fwd_strided",
     "SattnError", "library", "LIB_PATH", "STATUS",
 ]
 
@@ -67,6 +67,9 @@ def library():
     lib.sattn_fwd_cache.restype = i32
     lib.sattn_fwd_cache.argtypes = [i32, vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64, i32,
                                     ctypes.c_float, vp]
+    lib.sattn_fwd_strided.restype = i32
+    lib.sattn_fwd_strided.argtypes = [i32, vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64,
+                                      ctypes.POINTER(i64), ctypes.POINTER(i64), i32, ctypes.c_float, vp]
     lib.sattn_fwd_split_cache.restype = i32
     lib.sattn_fwd_split_cache.argtypes = [i32, vp, vp, vp, fp, fp, fp, i64, i64, i64, i64, i64, i64, i64,
                                           i32, ctypes.c_float, vp]
@@ -170,6 +173,42 @@ def sattn_fwd_cache(q, k, v, causal=False, scale=None, out=None, lse=None):
     with torch.cuda.device(dev):
         _check(lib.sattn_fwd_cache(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                    b, hq, hkv, nq, nk, d, int(bool(causal)), _scale(scale, d), _stream(dev)))
+    return out, lse
+
+
+def sattn_fwd_strided(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """``sattn_fwd_cache`` on strided views: q [B,Hq,Nq,D] and k, v [B,Hkv,Nk,D]
+    may be transposed, sliced or expanded (stride 0) views whose last dim is
+    contiguous; k and v must have equal strides. They are read in place.
+
+    Returns dense (o [B,Hq,Nq,D], lse [B,Hq,Nq] float32)."""
+    lib = library()
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 4:
+            raise ValueError("%s must be a 4-dim GPU tensor" % name)
+        if t.shape[3] > 1 and t.stride(3) != 1:
+            raise ValueError("%s must have a contiguous last dim" % name)
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    b, hq, nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != b or k.shape[3] != d:
+        raise ValueError("k/v must be [B, Hkv, Nk, D] matching q")
+    if k.stride()[:3] != v.stride()[:3]:
+        raise ValueError("k and v must have equal strides")
+    hkv, nk = k.shape[1], k.shape[2]
+    dev = _same_device(q, k, v, out, lse)
+    out = torch.empty(q.shape, dtype=q.dtype, device=dev) if out is None else _dev_tensor(out, "out", q.dtype, 4)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=dev) if lse is None else \
+        _dev_tensor(lse, "lse", torch.float32, 3)
+    if out.shape != q.shape or lse.shape != (b, hq, nq):
+        raise ValueError("out/lse shape mismatch")
+    qs = (ctypes.c_int64 * 3)(*q.stride()[:3])
+    ks = (ctypes.c_int64 * 3)(*k.stride()[:3])
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else ctypes.c_void_p(0)  # noqa: E731
+    with torch.cuda.device(dev):
+        _check(lib.sattn_fwd_strided(_DTYPE_CODE[q.dtype], ptr(q), ptr(k), ptr(v), _ptr(out), _ptr(lse),
+                                     b, hq, hkv, nq, nk, d, qs, ks, int(bool(causal)), _scale(scale, d),
+                                     _stream(dev)))
     return out, lse
 
 

@@ -52,6 +52,10 @@ struct FwdParams {
   int nk;          // split, cache: Nk
   int off;         // split, cache: Nk - Nq, the logical position of query 0
   int pack;        // split: 1 = a slice is (batch, KV head) holding the Hq/Hkv query heads' rows
+  // cache: element strides of the batch, head and row dims of q and of k/v
+  // (k and v share them; the head dim d has stride 1). o and lse are dense.
+  int64_t qs_b, qs_h, qs_n;
+  int64_t ks_b, ks_h, ks_n;
   int chunk;       // split: keys per chunk
   int nchunks;     // split: C
   int nqt;         // query tiles per slice (dense/split) or per longest sequence (varlen)
@@ -69,6 +73,7 @@ struct Work {
   uint16_t* o;         // row 0 of this query tile
   float* lse;          // lse of row 0 of this query tile (stride 1 per row)
   int64_t q_rs;        // row strides in elements
+  int64_t o_rs;
   int64_t kv_rs;
   int q_pos0;          // logical position of row 0 (pos_mod > 0: of every row with (row0 + r) % pos_mod == 0)
   int pos_mod;         // 0: row r sits at q_pos0 + r; else at q_pos0 + (row0 + r) % pos_mod
@@ -117,6 +122,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.k = p.k + base;
     w.v = p.v + base;
     w.q_rs = D;
+    w.o_rs = D;
     w.kv_rs = D;
     w.lse = p.lse + (int64_t)head * p.n + w.q_pos0;
     w.k_begin = 0;
@@ -148,6 +154,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.nq = min(BM, len - w.q_pos0);
     const int g = h / (p.hq / p.hkv);
     w.q_rs = (int64_t)p.hq * D;
+    w.o_rs = w.q_rs;
     w.kv_rs = (int64_t)p.hkv * D;
     w.q = p.q + (int64_t)(a + w.q_pos0) * w.q_rs + (int64_t)h * D;
     w.o = p.o + (int64_t)(a + w.q_pos0) * w.q_rs + (int64_t)h * D;
@@ -175,13 +182,15 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     const int64_t qslice = ((int64_t)b * p.hq + h) * p.n;
     w.nq = min(BM, p.n - row0);
     w.q_pos0 = row0 + p.off;
-    w.q = p.q + (qslice + row0) * D;
+    w.q = p.q + b * p.qs_b + h * p.qs_h + row0 * p.qs_n;
     w.o = p.o + (qslice + row0) * D;
     w.lse = p.lse + qslice + row0;
-    w.k = p.k + (int64_t)kvs * p.nk * D;
-    w.v = p.v + (int64_t)kvs * p.nk * D;
-    w.q_rs = D;
-    w.kv_rs = D;
+    const int64_t kvbase = b * p.ks_b + (int64_t)(kvs % p.hkv) * p.ks_h;
+    w.k = p.k + kvbase;
+    w.v = p.v + kvbase;
+    w.q_rs = p.qs_n;
+    w.o_rs = D;
+    w.kv_rs = p.ks_n;
     w.k_begin = 0;
     // causal: keys after the tile's last query are never eligible; a tile
     // whose queries all precede the cache has no key at all
@@ -223,6 +232,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.k = p.k + kvbase;
     w.v = p.v + kvbase;
     w.q_rs = D;
+    w.o_rs = D;
     w.kv_rs = D;
     w.k_begin = c * p.chunk;
     w.k_end = min(p.nk, w.k_begin + p.chunk);
@@ -549,7 +559,7 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
     if (!row_ok) return;
     // an empty row (no eligible key) gives O = 0 and lse = -inf
     const float inv = (EMPTY_ROWS && lt == 0.f) ? 0.f : 1.f / lt;
-    uint16_t* op = w.o + (int64_t)qrow * w.q_rs;
+    uint16_t* op = w.o + (int64_t)qrow * w.o_rs;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -323,25 +323,46 @@ int sattn_fwd_split_cache(int dtype, const void* q, const void* k, const void* v
                     stream);
 }
 
-int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                    int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
-                    void* stream) {
+// Queries against a K/V cache with explicit element strides (batch, head,
+// row) for q and for k/v; o and lse are dense [B, Hq, Nq, D] / [B, Hq, Nq].
+static int cache_impl(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, const int64_t* qs,
+                      const int64_t* ks, int causal, float scale, void* stream) {
   int st = check_common(dtype, D, scale);
   if (st) return st;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return fail(SATTN_ERR_SHAPE, "negative size");
   if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return fail(SATTN_ERR_SHAPE, "Hq must be a multiple of Hkv");
-  int64_t qrows, kvrows, qbytes, kvbytes;
-  if (!product({B, Hq, Nq}, &qrows) || !product({B, Hkv, Nk}, &kvrows) || !product({qrows, D, 2}, &qbytes) ||
-      !product({kvrows, D, 2}, &kvbytes))
-    return fail(SATTN_ERR_SHAPE, "size overflow");
+  for (int i = 0; i < 3; ++i)
+    if (qs[i] < 0 || ks[i] < 0 || qs[i] % 8 != 0 || ks[i] % 8 != 0)
+      return fail(SATTN_ERR_ALIGN, "strides must be >= 0 and multiples of 8 elements (16 bytes)");
+  int64_t qrows, obytes;
+  if (!product({B, Hq, Nq}, &qrows) || !product({qrows, D, 2}, &obytes)) return fail(SATTN_ERR_SHAPE, "size overflow");
   if (qrows == 0) return ok();
   if (Nq >= kMaxLen || Nk >= kMaxLen || B * Hq >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "size too large");
-  if (Nk * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
-  if (!q || !o || !lse || (kvbytes > 0 && (!k || !v))) return fail(SATTN_ERR_NULL, "null pointer");
+  // k/v rows must not overlap: a tile's buffer range ends at its last row,
+  // and reads past it return zeros
+  if (Nk > 0 && ks[2] < D) return fail(SATTN_ERR_UNSUPPORTED, "k/v row stride must be >= D elements");
+  // extent of a strided tensor: last element offset + 1, in elements
+  int64_t qext = D, kext = 0;
+  {
+    int64_t a, b2, c;
+    if (!product({B - 1, qs[0]}, &a) || !product({Hq - 1, qs[1]}, &b2) || !product({Nq - 1, qs[2]}, &c))
+      return fail(SATTN_ERR_SHAPE, "size overflow");
+    qext += a + b2 + c;
+    if (Nk > 0) {
+      if (!product({B - 1, ks[0]}, &a) || !product({Hkv - 1, ks[1]}, &b2) || !product({Nk - 1, ks[2]}, &c))
+        return fail(SATTN_ERR_SHAPE, "size overflow");
+      kext = a + b2 + c + D;
+    }
+    if (qext < 0 || kext < 0 || qext > (int64_t(1) << 61) || kext > (int64_t(1) << 61))
+      return fail(SATTN_ERR_SHAPE, "size overflow");
+  }
+  if (Nk * ks[2] * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice spans 2 GiB or more");
+  if (!q || !o || !lse || (kext > 0 && (!k || !v))) return fail(SATTN_ERR_NULL, "null pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return fail(SATTN_ERR_ALIGN, "q/k/v/o need 16-byte and lse 4-byte alignment");
-  Range ins[3] = {range_of(q, qbytes, "q"), range_of(k, kvbytes, "k"), range_of(v, kvbytes, "v")};
-  Range outs[2] = {range_of(o, qbytes, "o"), range_of(lse, qrows * 4, "lse")};
+  Range ins[3] = {range_of(q, qext * 2, "q"), range_of(k, kext * 2, "k"), range_of(v, kext * 2, "v")};
+  Range outs[2] = {range_of(o, obytes, "o"), range_of(lse, qrows * 4, "lse")};
   if ((st = check_alias(ins, 3, outs, 2))) return st;
   const int bm = tile_m<MODE_CACHE>(D);
   const int64_t nqt = (Nq + bm - 1) / bm;
@@ -360,8 +381,34 @@ int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void
   p.nk = (int)Nk;
   p.off = (int)(Nk - Nq);
   p.nqt = (int)nqt;
+  p.qs_b = qs[0];
+  p.qs_h = qs[1];
+  p.qs_n = qs[2];
+  p.ks_b = ks[0];
+  p.ks_h = ks[1];
+  p.ks_n = ks[2];
   dispatch_fwd<MODE_CACHE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
   return launch_status();
+}
+
+int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                    int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale,
+                    void* stream) {
+  if (Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || D < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  int64_t qs[3], ks[3];
+  if (!product({Hq, Nq, D}, &qs[0]) || !product({Hkv, Nk, D}, &ks[0])) return fail(SATTN_ERR_SHAPE, "size overflow");
+  qs[1] = Nq * D;
+  qs[2] = D;
+  ks[1] = Nk * D;
+  ks[2] = D;
+  return cache_impl(dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, qs, ks, causal, scale, stream);
+}
+
+int sattn_fwd_strided(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, const int64_t* q_strides,
+                      const int64_t* kv_strides, int causal, float scale, void* stream) {
+  if (!q_strides || !kv_strides) return fail(SATTN_ERR_NULL, "null stride array");
+  return cache_impl(dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, q_strides, kv_strides, causal, scale, stream);
 }
 
 int sattn_merge(int dtype, const float* part_m, const float* part_l, const float* part_acc, int64_t rows, int64_t C,

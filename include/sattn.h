@@ -171,6 +171,30 @@ int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void
                     int causal, float scale, void* stream);
 
 /*
+ * sattn_fwd_cache on strided, sliced, transposed or broadcast read-only
+ * inputs, loaded in place ("Intermediate and advanced extension", workshop
+ * table, strided-softmax row: address both strides and accept transposed,
+ * sliced and broadcast read-only inputs; "Intermediate and advanced workshop
+ * validation": direct loads against copy-then-kernel).
+ *
+ *   q_strides  : host int64[3], element strides of q's batch, head and row
+ *                dims (q[b, h, i, d] at q + b*s[0] + h*s[1] + i*s[2] + d).
+ *   kv_strides : host int64[3], the same for k and v, which share them
+ *                (k and v may still be different tensors).
+ *   o, lse     : dense [B, Hq, Nq, D] and [B, Hq, Nq], as in sattn_fwd_cache.
+ * The head dim d is contiguous. Every stride must be >= 0 and a multiple of
+ * 8 elements (16 bytes); 0 broadcasts a dim. The k/v row stride must be >= D
+ * (k/v rows do not overlap) and Nk * (k/v row stride) * 2 bytes < 2^31; q
+ * rows may overlap.
+ * Alias checks use each input's extent: the last addressed element + 1.
+ * Alignment, causal rule, GQA map and empty rows as in sattn_fwd_cache.
+ */
+int sattn_fwd_strided(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                      const int64_t* q_strides, const int64_t* kv_strides,
+                      int causal, float scale, void* stream);
+
+/*
  * Split-KV partial states against a key/value cache, optionally causal:
  * sattn_fwd_split with the alignment of sattn_fwd_cache (query i at logical
  * position i + (Nk - Nq)). Same shapes, buffers and merge as sattn_fwd_split;

@@ -201,3 +201,22 @@ def test_split_cache_rejects(lib):
     assert call(pm=FAKE) == "SATTN_ERR_ALIAS"
     assert call(pm=NULL) == "SATTN_ERR_NULL"
     assert call(nq=0, pm=NULL) == "SATTN_OK"
+
+
+def test_strided_rejects(lib):
+    Arr = ctypes.c_int64 * 3
+
+    def call(qs=(8192, 1024, 128), ks=(8192, 1024, 128), **kw):
+        a = dict(b=1, hq=4, hkv=2, nq=8, nk=8, d=128, q=FAKE, k=FAKE2, v=FAKE3, o=FAKE4, lse=FAKE5)
+        a.update(kw)
+        return STATUS[lib.sattn_fwd_strided(1, a["q"], a["k"], a["v"], a["o"], a["lse"], a["b"], a["hq"], a["hkv"],
+                                            a["nq"], a["nk"], a["d"], Arr(*qs) if qs else None,
+                                            Arr(*ks) if ks else None, 1, F32(0.1), NULL)]
+    assert call(qs=(8192, 1024, 130)) == "SATTN_ERR_ALIGN"          # row stride not 16-byte aligned
+    assert call(ks=(8192, -1024, 128)) == "SATTN_ERR_ALIGN"         # negative stride
+    assert call(ks=(8192, 1024, 0)) == "SATTN_ERR_UNSUPPORTED"      # k/v rows must advance
+    assert call(ks=(8192, 1024, 64)) == "SATTN_ERR_UNSUPPORTED"     # ... by at least D
+    assert call(ks=(8192, 1024, 1 << 24), nk=100) == "SATTN_ERR_UNSUPPORTED"   # slice spans >= 2 GiB
+    assert call(qs=None) == "SATTN_ERR_NULL"
+    assert call(o=ctypes.c_void_p(0x10000 + 4096)) == "SATTN_ERR_ALIAS"   # o starts inside q (extent 8 KiB)
+    assert call(nq=0, q=NULL, k=NULL, v=NULL, o=NULL, lse=NULL) == "SATTN_OK"

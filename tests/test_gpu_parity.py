@@ -13,7 +13,8 @@ import torch
 
 import workloads as W
 from exact_tiled_attention_sattn_amd import (sattn_fwd, sattn_fwd_split, sattn_merge, sattn_fwd_varlen,
-                                             sattn_fwd_cache, sattn_fwd_split_cache, SattnError)
+                                             sattn_fwd_cache, sattn_fwd_split_cache, sattn_fwd_strided,
+                                             SattnError)
 from oracle import dense
 from tests.parity import check_attention, check_o, check_lse, TOL
 
@@ -567,3 +568,56 @@ def test_split_cache_noncausal_is_split_bitwise():
     torch.cuda.synchronize()
     for x, y in zip(a, b_):
         assert torch.equal(x, y)
+
+
+# ---------------------------------------------- strided, sliced, broadcast
+def _strided_views(kind, b, hq, hkv, nq, nk, d, dt, seed):
+    """Views q [B,Hq,Nq,D], k, v [B,Hkv,Nk,D] of the given layout kind (last
+    dim contiguous), built on the GPU from seeded values."""
+    g = torch.Generator().manual_seed(seed)
+    rnd = lambda *s: W.randn(s, dt, g).to(DEV)  # noqa: E731
+    if kind == "transposed":            # [B, N, H, D] storage
+        q = rnd(b, nq, hq, d).permute(0, 2, 1, 3)
+        k = rnd(b, nk, hkv, d).permute(0, 2, 1, 3)
+        v = rnd(b, nk, hkv, d).permute(0, 2, 1, 3)
+    elif kind == "sliced":              # the first D of a wider last dim; every other row
+        q = rnd(b, hq, 2 * nq, d + 64)[:, :, ::2, :d]
+        k = rnd(b, hkv, nk, d + 32)[..., 16:16 + d]
+        v = rnd(b, hkv, nk, d + 32)[..., 16:16 + d]
+    elif kind == "broadcast":           # one K/V for every batch entry, one q row set for every head
+        q = rnd(b, 1, nq, d).expand(b, hq, nq, d)
+        k = rnd(1, hkv, nk, d).expand(b, hkv, nk, d)
+        v = rnd(1, hkv, nk, d).expand(b, hkv, nk, d)
+    else:                               # packed qkv [B, N, 3, H, D] (Hq = Hkv)
+        x = rnd(b, nq, 3, hq, d)
+        q, k, v = (x[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    return q, k, v
+
+
+STRIDED = [
+    ("transposed", 2, 8, 2, 300, 300, 128, "bf16"),
+    ("transposed", 1, 4, 4, 100, 257, 64, "fp16"),
+    ("sliced", 1, 4, 2, 129, 400, 128, "fp16"),
+    ("broadcast", 3, 4, 2, 70, 190, 64, "bf16"),
+    ("packed", 2, 4, 4, 333, 333, 128, "bf16"),
+    ("packed", 1, 2, 2, 65, 65, 32, "fp16"),
+]
+
+
+@pytest.mark.parametrize("kind,b,hq,hkv,nq,nk,d,dt", STRIDED)
+@pytest.mark.parametrize("causal", [False, True])
+def test_strided_inputs(kind, b, hq, hkv, nq, nk, d, dt, causal):
+    _banner("strided", kind, b, hq, hkv, nq, nk, d, dt, causal)
+    q, k, v = _strided_views(kind, b, hq, hkv, nq, nk, d, dt, seed=7000 + nq + d)
+    assert not (q.is_contiguous() and k.is_contiguous())
+    scale = W.scale_f32(d)
+    q0, k0, v0 = (x.clone() for x in (q, k, v))
+    o, lse = sattn_fwd_strided(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.attention_cache(W.to_f64(q.cpu()), W.to_f64(k.cpu()), W.to_f64(v.cpu()), scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "strided " + kind)
+    # inputs untouched; same bits as the dense-layout call on contiguous copies
+    assert torch.equal(q, q0) and torch.equal(k, k0) and torch.equal(v, v0)
+    o2, l2 = sattn_fwd_cache(q.contiguous(), k.contiguous(), v.contiguous(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)

@@ -233,3 +233,93 @@ def merge_partials(m, l, acc):
     o = np.where(nonempty[..., None], o, 0.0)
     lse = np.where(nonempty, lse, NEG_INF)
     return o, lse
+
+
+def sparse_eligibility(nq, nk, causal=False, left=-1, right=-1, n_global=0, block_mask=None, block_q=64,
+                       block_k=64):
+    """Element eligibility [Nq, Nk] of the changed (sparse) operators, for
+    queries at positions i + (Nk - Nq) (``cache_positions``).
+
+    Window and global tokens ("Attention algorithms and data movement",
+    lesson 07; the rule is this build's reading): key j is eligible for the
+    query at position p iff it lies in the window p - left <= j <= p + right
+    (a negative bound is unlimited), or j < n_global (a global key, visible
+    to every query), or p < n_global (a global query sees every key). The
+    three sets are united, so a pair is counted once however many of them
+    hold it.
+    Block sparsity (lesson 06): block_mask [nqb, nkb] (nonzero = active)
+    keeps pair (i, j) only if block (i // block_q, j // block_k) is active;
+    the mask rows are indexed by query index i, not by position.
+    Causal: additionally j <= p. All conditions are intersected.
+    """
+    p = cache_positions(nq, nk)[:, None]
+    j = np.arange(nk)[None, :]
+    win = np.ones((nq, nk), dtype=bool)
+    if left >= 0:
+        win &= j >= p - left
+    if right >= 0:
+        win &= j <= p + right
+    ok = win | (j < n_global) | (p < n_global)
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        ok &= bm[np.arange(nq)[:, None] // block_q, j // block_k]
+    if causal:
+        ok &= j <= p
+    return ok
+
+
+def attention_allowed(q, k, v, scale, allowed):
+    """Softmax attention of one head over an explicit eligibility mask
+    ``allowed`` [Nq, Nk]; a row with no eligible key is the empty row
+    (O = 0, lse = -inf). The plain definition with the mask applied."""
+    nq = q.shape[0]
+    o = np.zeros((nq, v.shape[1]), dtype=np.float64)
+    lse = np.full((nq,), NEG_INF, dtype=np.float64)
+    if nq == 0 or k.shape[0] == 0:
+        return o, lse
+    s = np.where(allowed, scale * (q @ k.T), NEG_INF)
+    m = s.max(axis=1)
+    nonempty = np.isfinite(m)
+    m_safe = np.where(nonempty, m, 0.0)
+    p = np.exp(s - m_safe[:, None])
+    l = p.sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o_all = (p @ v) / np.where(nonempty, l, 1.0)[:, None]
+        lse_all = m_safe + np.log(np.where(nonempty, l, 1.0))
+    o[nonempty] = o_all[nonempty]
+    lse[nonempty] = lse_all[nonempty]
+    return o, lse
+
+
+def attention_sparse(q, k, v, scale, causal=False, left=-1, right=-1, n_global=0, block_mask=None, block_q=64,
+                     block_k=64, rows=None):
+    """The matching sparse reference: exact softmax attention restricted to
+    ``sparse_eligibility`` (lessons 06 and 07: a changed operator, not an
+    approximation of dense attention).
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D], KV head h // (Hq / Hkv).
+    block_mask: None, [nqb, nkb] (every head) or [Hq, nqb, nkb] (per query
+    head). ``rows``: optional [B, Hq, R] query indices. Returns o, lse as
+    ``attention_cache``.
+    """
+    b_, hq, nq = q.shape[0], q.shape[1], q.shape[2]
+    hkv, nk = k.shape[1], k.shape[2]
+    group = hq // hkv
+    bm = None if block_mask is None else np.asarray(block_mask)
+    r_count = nq if rows is None else np.asarray(rows).shape[2]
+    o = np.zeros((b_, hq, r_count, v.shape[3]), dtype=np.float64)
+    lse = np.full((b_, hq, r_count), NEG_INF, dtype=np.float64)
+    masks = {}
+    for h in range(hq):
+        key = 0 if (bm is None or bm.ndim == 2) else h
+        if key not in masks:
+            masks[key] = sparse_eligibility(nq, nk, causal, left, right, n_global,
+                                            None if bm is None else (bm if bm.ndim == 2 else bm[h]),
+                                            block_q, block_k)
+    for b in range(b_):
+        for h in range(hq):
+            g = h // group
+            allowed = masks[0 if (bm is None or bm.ndim == 2) else h]
+            r = np.arange(nq) if rows is None else np.asarray(rows)[b, h]
+            o[b, h], lse[b, h] = attention_allowed(q[b, h][r], k[b, g], v[b, g], scale, allowed[r])
+    return o, lse

@@ -119,8 +119,36 @@ def _dense_checks(d):
         o_ref = F.scaled_dot_product_attention(qt[2:], kt, vt, attn_mask=mask[2:], scale=0.5).numpy()
         return np.allclose(o[2:], o_ref, rtol=1e-12, atol=1e-12)
 
+    def sparse():
+        # causal window of 3 keys united with 2 global tokens: closed-form
+        # pair count and one-key-window closed form, then a block mask that
+        # is not symmetric against torch SDPA with the brute-force mask
+        n = 20
+        m = d.sparse_eligibility(n, n, causal=True, left=2, n_global=2)
+        want = sum(i + 1 if i < 2 else min(i + 1, 3) + 2 - max(0, 2 - max(0, i - 2)) for i in range(n))
+        if int(m.sum()) != want:
+            return False
+        # non-causal band of +-1 with 2 global tokens: the global queries see
+        # all n keys; any other row sees its band plus the globals outside it
+        m = d.sparse_eligibility(n, n, left=1, right=1, n_global=2)
+        band = lambda i: set(range(max(0, i - 1), min(n, i + 2)))  # noqa: E731
+        want = sum(n if i < 2 else len(band(i) | {0, 1}) for i in range(n))
+        if int(m.sum()) != want:
+            return False
+        rng = np.random.default_rng(7)
+        q, k, v = (rng.standard_normal((1, 1, 12, 3)) for _ in range(3))
+        o, _ = d.attention_sparse(q, k, v, 0.5, causal=True, left=0)
+        if not np.allclose(o[0, 0], v[0, 0], rtol=1e-13, atol=1e-14):
+            return False
+        bm = np.array([[1, 0, 0], [1, 1, 0], [0, 0, 1]], dtype=np.uint8)   # rows of 4 queries, 4 keys
+        o, _ = d.attention_sparse(q, k, v, 0.5, block_mask=bm, block_q=4, block_k=4)
+        allowed = torch.tensor([[bool(bm[i // 4][j // 4]) for j in range(12)] for i in range(12)])
+        qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+        o_ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed, scale=0.5).numpy()
+        return np.allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+
     for name, fn in (("golden", golden), ("sdpa", sdpa), ("gqa", gqa), ("split", split), ("cache", cache),
-                     ("causal_split", causal_split)):
+                     ("causal_split", causal_split), ("sparse", sparse)):
         try:
             ok = bool(fn())
         except Exception:
@@ -147,6 +175,13 @@ DENSE_MUTANTS = [
     ("top-left alignment", "return np.arange(nq, dtype=np.int64) + (nk - nq)", "return np.arange(nq, dtype=np.int64)"),
     ("alignment off by one", "return np.arange(nq, dtype=np.int64) + (nk - nq)",
      "return np.arange(nq, dtype=np.int64) + (nk - nq - 1)"),
+    ("global tokens intersected, not united", "ok = win | (j < n_global) | (p < n_global)",
+     "ok = win & ((j < n_global) | (p < n_global))"),
+    ("globals counted only as keys", "ok = win | (j < n_global) | (p < n_global)", "ok = win | (j < n_global)"),
+    ("window left bound off by one", "win &= j >= p - left", "win &= j > p - left"),
+    ("block mask transposed", "ok &= bm[np.arange(nq)[:, None] // block_q, j // block_k]",
+     "ok &= bm[j // block_k, np.arange(nq)[:, None] // block_q]"),
+    ("sparse causal dropped", "    if causal:\n        ok &= j <= p\n", ""),
     ("partial numerator without weights", "acc[:, c, :] = p @ v[j0:j1]", "acc[:, c, :] = v[j0:j1].sum(axis=0)"),
 ]
 

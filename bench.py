@@ -60,7 +60,7 @@ def dense_flops(b, h, n, d, causal):
     return (2 if causal else 4) * b * h * n * n * d
 
 
-def gate_rows(o, lse, q, k, v, scale, causal, rows, pos, dtype, what):
+def gate_rows(o, lse, q, k, v, scale, causal, rows, pos, dtype, what, allowed=None):
     """Correctness gate for one (batch, head) slice: the GPU's rows ``rows``
     (query indices) against float64 torch on the host, computed directly from
     the definition for those rows only (``pos``: their logical positions,
@@ -72,6 +72,8 @@ def gate_rows(o, lse, q, k, v, scale, causal, rows, pos, dtype, what):
     s = scale * (qh @ kh.T)
     if causal:
         s = s.masked_fill(torch.arange(kh.shape[0])[None, :] > torch.as_tensor(pos)[:, None], -math.inf)
+    if allowed is not None:                 # [R, Nk] eligibility of the gated rows
+        s = s.masked_fill(~allowed, -math.inf)
     lse_ref = torch.logsumexp(s, dim=-1)
     o_ref = torch.exp(s - lse_ref[:, None]) @ vh
     return check_attention(o[rows], lse[rows], o_ref.numpy(), lse_ref.numpy(), dtype, what)
@@ -349,6 +351,65 @@ def strided_extra(steps):
     return res
 
 
+def sparse_extra(steps):
+    """Changed operators (lessons 06 and 07): work counts kept (query, key)
+    pairs at 4*D FLOP each.
+    * causal sliding window of 2048 keys united with 64 global tokens,
+      B=1, H=16, N=16384, D=128 bf16;
+    * block-sparse, non-causal, 64x64 blocks, a seeded per-head mask with a
+      quarter of the blocks active, B=1, H=16, N=8192, D=128 bf16."""
+    from exact_tiled_attention_sattn_amd import sattn_fwd_sparse
+    res = {}
+    h, d = 16, 128
+    scale = W.scale_f32(d)
+    # -- window + globals
+    n, w, ng = 16384, 2048, 64
+    q, k, v = (x.to(DEV) for x in W.qkv((1, h, n, d), (1, h, n, d), "bf16", 10))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, h, n), dtype=torch.float32, device=DEV)
+    fn = lambda: sattn_fwd_sparse(q, k, v, causal=True, window=(w - 1, -1), n_global=ng, scale=scale,  # noqa: E731
+                                  out=o, lse=lse)
+    fn()
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 63, 64, 5000, n - 1])
+    j = torch.arange(n)[None, :]
+    p = rows[:, None]
+    allowed = (j <= p) & ((j >= p - (w - 1)) | (j < ng) | (p < ng))
+    gate_rows(o[0, 3].cpu(), lse[0, 3].cpu(), q[0, 3], k[0, 3], v[0, 3], scale, False, rows, None, torch.bfloat16,
+              "gate window", allowed=allowed)
+    ms = float(np.mean(time_launches(fn, steps, 2)))
+    pairs = sum((i + 1) if i < ng else min(i + 1, w) + ng - max(0, ng - max(0, i - w + 1)) for i in range(n)) * h
+    res["causal_window2048_global64_16x16384x128_bf16"] = {
+        "ms_mean": ms, "kept_pairs": pairs, "TFLOPs": 4 * d * pairs / ms / 1e9,
+        "frac_of_bf16_peak": 4 * d * pairs / ms / 1e9 / PEAK_BF16_TFLOPS}
+    del q, k, v, o
+    # -- block sparse
+    n = 8192
+    q, k, v = (x.to(DEV) for x in W.qkv((1, h, n, d), (1, h, n, d), "bf16", 11))
+    gen = torch.Generator().manual_seed(11)
+    bm = (torch.rand((h, n // 64, n // 64), generator=gen) < 0.25).to(torch.uint8)
+    bmd = bm.to(DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, h, n), dtype=torch.float32, device=DEV)
+    fn = lambda: sattn_fwd_sparse(q, k, v, block_mask=bmd, block_q=64, block_k=64, scale=scale,  # noqa: E731
+                                  out=o, lse=lse)
+    fn()
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 4000, n - 1])
+    allowed = bm[5][rows // 64].repeat_interleave(64, dim=1).bool()
+    ok = allowed.any(dim=1)
+    gate_rows(o[0, 5].cpu(), lse[0, 5].cpu(), q[0, 5], k[0, 5], v[0, 5], scale, False, rows[ok], None,
+              torch.bfloat16, "gate block-sparse", allowed=allowed[ok])
+    ms = float(np.mean(time_launches(fn, steps, 2)))
+    pairs = int(bm.sum()) * 64 * 64
+    res["block_sparse_quarter_64x64_16x8192x128_bf16"] = {
+        "ms_mean": ms, "active_block_pairs": int(bm.sum()), "kept_pairs": pairs,
+        "TFLOPs": 4 * d * pairs / ms / 1e9, "frac_of_bf16_peak": 4 * d * pairs / ms / 1e9 / PEAK_BF16_TFLOPS}
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(budget_s):
     """The FP64 oracle on sampled query rows of the batched workload, both
     variants, on the host cores, scaled to TFLOP/s by the sampled fraction."""
@@ -513,6 +574,8 @@ def main():
         extras["cache_gqa_decode"] = gqa_decode_extra(max(3, min(args.steps, 10)))
         log("strided (transposed) inputs")
         extras["strided_transposed"] = strided_extra(max(3, min(args.steps, 10)))
+        log("sparse: window + globals, block mask")
+        extras["sparse"] = sparse_extra(max(3, min(args.steps, 10)))
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

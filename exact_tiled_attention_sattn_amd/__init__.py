@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen", "sattn_fwd_cache",
-    "sattn_fwd_split_cache", "sattn_fwd_strided",
+    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse",
     "SattnError", "library", "LIB_PATH", "STATUS",
 ]
 
@@ -70,6 +70,9 @@ def library():
     lib.sattn_fwd_strided.restype = i32
     lib.sattn_fwd_strided.argtypes = [i32, vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64,
                                       ctypes.POINTER(i64), ctypes.POINTER(i64), i32, ctypes.c_float, vp]
+    lib.sattn_fwd_sparse.restype = i32
+    lib.sattn_fwd_sparse.argtypes = [i32, vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64, i32, i64, i64, i64,
+                                     vp, i64, i64, i64, ctypes.c_float, vp]
     lib.sattn_fwd_split_cache.restype = i32
     lib.sattn_fwd_split_cache.argtypes = [i32, vp, vp, vp, fp, fp, fp, i64, i64, i64, i64, i64, i64, i64,
                                           i32, ctypes.c_float, vp]
@@ -209,6 +212,42 @@ def sattn_fwd_strided(q, k, v, causal=False, scale=None, out=None, lse=None):
         _check(lib.sattn_fwd_strided(_DTYPE_CODE[q.dtype], ptr(q), ptr(k), ptr(v), _ptr(out), _ptr(lse),
                                      b, hq, hkv, nq, nk, d, qs, ks, int(bool(causal)), _scale(scale, d),
                                      _stream(dev)))
+    return out, lse
+
+
+def sattn_fwd_sparse(q, k, v, causal=False, window=(-1, -1), n_global=0, block_mask=None, block_q=64, block_k=64,
+                     scale=None, out=None, lse=None):
+    """Sparse attention: ``sattn_fwd_cache`` restricted to the window
+    (left, right) (-1 = unlimited), ``n_global`` global tokens and an optional
+    uint8 block mask [Hq or 1, ceil(Nq/block_q), ceil(Nk/block_k)] on the GPU.
+
+    Returns (o [B,Hq,Nq,D], lse [B,Hq,Nq] float32)."""
+    lib = library()
+    b, hq, nq, d, hkv, nk = _cache_shapes(q, k, v)
+    dev = _same_device(q, k, v, out, lse, block_mask)
+    heads = 0
+    if block_mask is not None:
+        _dev_tensor(block_mask, "block_mask", torch.uint8)
+        if block_mask.dim() == 2:
+            heads = 1
+            block_mask = block_mask.unsqueeze(0)
+        if block_mask.dim() != 3:
+            raise ValueError("block_mask must be [nqb, nkb] or [heads, nqb, nkb]")
+        heads = block_mask.shape[0]
+        nqb, nkb = -(-nq // int(block_q)), -(-nk // int(block_k))
+        if tuple(block_mask.shape[1:]) != (nqb, nkb):
+            raise ValueError("block_mask must be [heads, %d, %d]" % (nqb, nkb))
+    out = torch.empty_like(q) if out is None else _dev_tensor(out, "out", q.dtype, 4)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=dev) if lse is None else \
+        _dev_tensor(lse, "lse", torch.float32, 3)
+    if out.shape != q.shape or lse.shape != (b, hq, nq):
+        raise ValueError("out/lse shape mismatch")
+    left, right = (int(x) for x in window)
+    with torch.cuda.device(dev):
+        _check(lib.sattn_fwd_sparse(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                    b, hq, hkv, nq, nk, d, int(bool(causal)), left, right, int(n_global),
+                                    _ptr(block_mask), heads, int(block_q), int(block_k), _scale(scale, d),
+                                    _stream(dev)))
     return out, lse
 
 

@@ -34,7 +34,12 @@ namespace sattn {
 // SPLIT: per-chunk partial states over a key range (optionally causal).
 // CACHE: [B, Hq, Nq, D] queries against a [B, Hkv, Nk, D] key/value cache;
 //        query i sits at logical position i + (Nk - Nq).
-enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_CACHE = 3 };
+// SPARSE: CACHE restricted to a sliding window, global tokens and a
+//        block mask; only the key tiles some row needs are visited.
+enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_CACHE = 3, MODE_SPARSE = 4 };
+
+// Key tiles a sparse workgroup may list (Nk <= 64 * kSparseMaxTiles).
+constexpr int kSparseMaxTiles = 1024;
 
 struct FwdParams {
   const uint16_t* q;
@@ -56,6 +61,15 @@ struct FwdParams {
   // (k and v share them; the head dim d has stride 1). o and lse are dense.
   int64_t qs_b, qs_h, qs_n;
   int64_t ks_b, ks_h, ks_n;
+  // sparse: key j is eligible for the query at position p iff
+  // (p - win_left <= j <= p + win_right, a negative bound unlimited) or
+  // j < n_global or p < n_global, and block (i / bm_q, j / bm_k) of the
+  // query index i is active in bmask (if given; head h reads the
+  // nqb x nkb bytes at bmask + h * bm_hstride), and j <= p when causal.
+  int win_left, win_right, n_global;
+  const uint8_t* bmask;
+  int bm_q, bm_k, bm_nkb;
+  int64_t bm_hstride;
   int chunk;       // split: keys per chunk
   int nchunks;     // split: C
   int nqt;         // query tiles per slice (dense/split) or per longest sequence (varlen)
@@ -81,6 +95,7 @@ struct Work {
   int nq;              // valid rows in this tile
   int k_begin, k_end;  // keys [k_begin, k_end) of the slice
   int64_t part_row0;   // split: index (slice_row * C + c) of row 0
+  const uint8_t* bmask;  // sparse: this head's block mask (or null)
 };
 
 // Spread of workgroups over the 8 XCDs: blocks are handed out round-robin by
@@ -165,7 +180,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.k_end = CAUSAL ? min(len, w.q_pos0 + BM) : len;
     w.pos_mod = 0;
     return true;
-  } else if constexpr (MODE == MODE_CACHE) {
+  } else if constexpr (MODE == MODE_CACHE || MODE == MODE_SPARSE) {
     // Logical order: (batch, KV head), then query tile (heaviest first), then
     // the query heads sharing that KV head, so that the workgroups reading
     // one cache slice run together on one XCD and its L2.
@@ -196,6 +211,12 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     // whose queries all precede the cache has no key at all
     w.k_end = CAUSAL ? min(p.nk, max(0, w.q_pos0 + BM)) : p.nk;
     w.pos_mod = 0;
+    if constexpr (MODE == MODE_SPARSE) {
+      w.row0 = row0;
+      w.bmask = p.bmask ? p.bmask + h * p.bm_hstride : nullptr;
+      if (p.win_right >= 0 && w.q_pos0 >= p.n_global)   // no global query: no row sees past p + win_right
+        w.k_end = min(w.k_end, max(0, w.q_pos0 + BM + p.win_right));
+    }
     return w.nq > 0;
   } else {
     // Split-KV: block id -> (slice, query tile, chunk), chunk fastest. A
@@ -295,7 +316,8 @@ __device__ __forceinline__ float sum_halves(float x) {
 // seen so far minus 8 stays in [0, 256]). The split path keeps the exact
 // chunk max because it is part of the partial-state output.
 template <class E, int D, int BN, int NW, bool CAUSAL, int MODE>
-__device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uint16_t* sbuf0, uint16_t* sbuf1) {
+__device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uint16_t* sbuf0, uint16_t* sbuf1,
+                                          int* tlist, int* tcount) {
   constexpr int PPR = D / 8;               // 16-byte pieces per row
   constexpr int TILE_BYTES = BN * D * 2;   // one K or V tile
   constexpr int NI = TILE_BYTES / 1024 / NW;  // 1 KiB direct loads per wave per tile
@@ -306,7 +328,8 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   // Rows that can have no eligible key in the keys walked here: queries
   // before the cache or an empty cache, or a causal chunk after a query. Their max stays -inf,
   // and exps are then taken against 0 so that masked scores give 0, not NaN.
-  constexpr bool EMPTY_ROWS = MODE == MODE_CACHE || (CAUSAL && MODE == MODE_SPLIT);
+  constexpr bool EMPTY_ROWS = MODE == MODE_CACHE || MODE == MODE_SPARSE || (CAUSAL && MODE == MODE_SPLIT);
+  constexpr bool SPARSE = MODE == MODE_SPARSE;
   constexpr float LAZY_TH = 8.0f;
   static_assert(NI >= 1 && TILE_BYTES % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
   static_assert(D % 32 == 0 && BN % 32 == 0, "tile shape");
@@ -410,15 +433,25 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
 
   // One tile: wait for its loads, start the next tile's loads into the other
   // buffer, then compute on this one.
-  auto step = [&](int t, const uint16_t* cur, uint16_t* nxt, auto mask_tag, auto fast_tag) {
+  // Sparse mode walks a list of the key tiles some wave needs (built below):
+  // entry = tile | (waves that need it) << 16 | (element mask needed) << 24.
+  int nact = 0;
+  auto step = [&](int idx, const uint16_t* cur, uint16_t* nxt, auto mask_tag, auto fast_tag) {
     constexpr bool MASKED = decltype(mask_tag)::value;
     constexpr bool FAST = decltype(fast_tag)::value;
+    const int e = SPARSE ? tlist[idx] : idx;
+    const int t = SPARSE ? (e & 0xffff) : idx;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t visible to all waves; every wave is done with tile t-1
-    if (t + 1 < ntiles) issue_tile(t + 1, nxt);
+    __syncthreads();  // tile t visible to all waves; every wave is done with the previous tile
+    if (SPARSE) {
+      if (idx + 1 < nact) issue_tile(tlist[idx + 1] & 0xffff, nxt);
+    } else if (t + 1 < ntiles) {
+      issue_tile(t + 1, nxt);
+    }
 
     const int kt0 = w.k_begin + t * BN;
     if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
+    if (SPARSE && !((e >> (16 + wave_u)) & 1)) return;   // this wave's query block or window skips the tile
     const uint16_t* sK = cur;
     const uint16_t* sV = cur + BN * D;
 
@@ -437,8 +470,10 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
       for (int kk = 0; kk < KK; ++kk) s[kb] = E::mfma32(ka[kb][kk], qreg[kk], s[kb]);
     }
 
-    // ---- mask: key tail, and keys after the query (diagonal kept)
-    if constexpr (MASKED) {
+    // ---- mask: key tail, and keys after the query (diagonal kept); in
+    // sparse mode also the window / global-token rule, only on listed tiles
+    // that some row does not wholly see
+    if constexpr (MASKED && !SPARSE) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -446,6 +481,21 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
           const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
           if ((key >= w.k_end) || (CAUSAL && key > my_pos)) s[kb][r] = -INFINITY;
         }
+    }
+    if constexpr (SPARSE) {
+      if ((e >> 24) & 1) {
+        const bool row_global = my_pos < p.n_global;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool in_win = (p.win_left < 0 || key >= my_pos - p.win_left) &&
+                                (p.win_right < 0 || key <= my_pos + p.win_right);
+            const bool ok = key < w.k_end && (!CAUSAL || key <= my_pos) && (in_win || key < p.n_global || row_global);
+            if (!ok) s[kb][r] = -INFINITY;
+          }
+      }
     }
 
     if constexpr (FAST) {
@@ -522,7 +572,61 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   if (CAUSAL) n_full = min(n_full, max(0, (w.q_pos0 - w.k_begin + 1) / BN));
   const std::integral_constant<bool, false> no{};
   const std::integral_constant<bool, true> yes{};
+  if constexpr (SPARSE) {
+    // Wave 0 lists the key tiles in order, 64 candidates per pass: a tile is
+    // kept if some wave needs it (its rows' window / global tokens reach the
+    // tile, the tile is not after their positions, and their query block's
+    // mask bit for the tile's key block is set), and flagged for element
+    // masks unless every row of every such wave sees all of its keys.
+    if (wave_u == 0) {
+      int count = 0;
+      for (int base = 0; base < ntiles; base += 64) {
+        const int t = base + lane;
+        int bits = 0;
+        bool full_all = true;
+        if (t < ntiles) {
+          const int k0 = w.k_begin + t * BN;
+          const int k1 = min(k0 + BN, w.k_end) - 1;
+          for (int wv = 0; wv < NW; ++wv) {
+            const int r0 = wv * 32;
+            if (r0 >= w.nq) break;
+            const int p0 = w.q_pos0 + r0;
+            const int p1 = w.q_pos0 + min(r0 + 32, w.nq) - 1;
+            const bool glob = k0 < p.n_global || p0 < p.n_global;
+            const bool win = (p.win_left < 0 || k1 >= p0 - p.win_left) && (p.win_right < 0 || k0 <= p1 + p.win_right);
+            bool need = (!CAUSAL || k0 <= p1) && (win || glob);
+            if (need && w.bmask)
+              need = w.bmask[(int64_t)((w.row0 + r0) / p.bm_q) * p.bm_nkb + k0 / p.bm_k] != 0;
+            if (!need) continue;
+            bits |= 1 << wv;
+            const bool win_full = (p.win_left < 0 || k0 >= p1 - p.win_left) && (p.win_right < 0 || k1 <= p0 + p.win_right);
+            const bool glob_full = k1 < p.n_global || p1 < p.n_global;
+            const bool full = (k0 + BN <= w.k_end) && (!CAUSAL || k1 <= p0) && (win_full || glob_full);
+            full_all = full_all && full;
+          }
+        }
+        const uint64_t act = __builtin_amdgcn_ballot_w64(bits != 0);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(act >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)act, 0));
+        if (bits != 0) tlist[count + below] = t | (bits << 16) | ((full_all ? 0 : 1) << 24);
+        count += __builtin_popcountll(act);
+      }
+      if (lane == 0) *tcount = count;
+    }
+    __syncthreads();
+    nact = *tcount;
+  }
   auto run = [&](auto fast_tag) {
+    if constexpr (SPARSE) {
+      if (nact == 0) return;
+      issue_tile(tlist[0] & 0xffff, sbuf0);
+      int n = 0;
+      for (; n + 1 < nact; n += 2) {
+        step(n, sbuf0, sbuf1, std::true_type{}, fast_tag);
+        step(n + 1, sbuf1, sbuf0, std::true_type{}, fast_tag);
+      }
+      if (n < nact) step(n, sbuf0, sbuf1, std::true_type{}, fast_tag);
+      return;
+    }
     if (ntiles == 0) return;
     issue_tile(0, sbuf0);
     if (n_full >= 1) step(0, sbuf0, sbuf1, no, no);
@@ -537,8 +641,8 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
       else step(t, sbuf0, sbuf1, yes, fast_tag);
     }
   };
-  if constexpr (MODE == MODE_SPLIT) {
-    run(no);  // the partial state exports the exact chunk max
+  if constexpr (MODE == MODE_SPLIT || SPARSE) {
+    run(no);  // the partial state exports the exact chunk max; a sparse row's first eligible key can come late
   } else {
     run(yes);
     if (__syncthreads_or(overflow ? 1 : 0)) {  // rare: redo with the exact update
@@ -597,13 +701,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
   // (otherwise it makes every LDS read wait for the in-flight prefetch).
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[2 * BN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[2 * BN * D];
+  __shared__ int tlist[MODE == MODE_SPARSE ? kSparseMaxTiles : 1];
+  __shared__ int tcount;
   constexpr int NITEMS = items_per_block<CAUSAL, MODE>();
 #pragma unroll 1
   for (int item = 0; item < NITEMS; ++item) {
     if (item > 0) __syncthreads();  // the previous tile's LDS reads are done
     Work w;
     if (!decode_work<D, BM, CAUSAL, MODE>(p, item, w)) continue;  // uniform over the workgroup
-    attn_rows<E, D, BN, NW, CAUSAL, MODE>(p, w, sbuf0, sbuf1);
+    attn_rows<E, D, BN, NW, CAUSAL, MODE>(p, w, sbuf0, sbuf1, tlist, &tcount);
   }
 }
 

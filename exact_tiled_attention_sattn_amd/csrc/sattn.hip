@@ -323,11 +323,19 @@ int sattn_fwd_split_cache(int dtype, const void* q, const void* k, const void* v
                     stream);
 }
 
+// Window / global-token / block-mask restriction of the sparse entry point.
+struct SparseSpec {
+  int64_t left, right, n_global;
+  const uint8_t* mask;
+  int64_t mask_heads, block_q, block_k;
+};
+
 // Queries against a K/V cache with explicit element strides (batch, head,
 // row) for q and for k/v; o and lse are dense [B, Hq, Nq, D] / [B, Hq, Nq].
+// With a sparse spec the same walk is restricted to it (MODE_SPARSE).
 static int cache_impl(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                       int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, const int64_t* qs,
-                      const int64_t* ks, int causal, float scale, void* stream) {
+                      const int64_t* ks, int causal, float scale, void* stream, const SparseSpec* sp = nullptr) {
   int st = check_common(dtype, D, scale);
   if (st) return st;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return fail(SATTN_ERR_SHAPE, "negative size");
@@ -361,10 +369,28 @@ static int cache_impl(int dtype, const void* q, const void* k, const void* v, vo
   if (!q || !o || !lse || (kext > 0 && (!k || !v))) return fail(SATTN_ERR_NULL, "null pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return fail(SATTN_ERR_ALIGN, "q/k/v/o need 16-byte and lse 4-byte alignment");
-  Range ins[3] = {range_of(q, qext * 2, "q"), range_of(k, kext * 2, "k"), range_of(v, kext * 2, "v")};
+  int64_t nkb = 0, mbytes = 0;
+  if (sp) {
+    if (Nk > int64_t(64) * kSparseMaxTiles)
+      return fail(SATTN_ERR_UNSUPPORTED, "sparse attention supports Nk <= %d", 64 * kSparseMaxTiles);
+    if (sp->left < -1 || sp->right < -1 || sp->n_global < 0 || sp->left >= kMaxLen || sp->right >= kMaxLen ||
+        sp->n_global >= kMaxLen)
+      return fail(SATTN_ERR_VALUE, "window bounds must be >= -1 and n_global >= 0");
+    if (sp->mask) {
+      if (sp->block_q <= 0 || sp->block_q % 32 != 0 || sp->block_k <= 0 || sp->block_k % 64 != 0 ||
+          sp->block_q >= kMaxLen || sp->block_k >= kMaxLen)
+        return fail(SATTN_ERR_UNSUPPORTED, "block_q must be a positive multiple of 32 and block_k of 64");
+      if (sp->mask_heads != 1 && sp->mask_heads != Hq) return fail(SATTN_ERR_SHAPE, "mask_heads must be 1 or Hq");
+      const int64_t nqb = (Nq + sp->block_q - 1) / sp->block_q;
+      nkb = (Nk + sp->block_k - 1) / sp->block_k;
+      if (!product({sp->mask_heads, nqb, nkb}, &mbytes)) return fail(SATTN_ERR_SHAPE, "size overflow");
+    }
+  }
+  Range ins[4] = {range_of(q, qext * 2, "q"), range_of(k, kext * 2, "k"), range_of(v, kext * 2, "v"),
+                  range_of(sp ? sp->mask : nullptr, mbytes, "block_mask")};
   Range outs[2] = {range_of(o, obytes, "o"), range_of(lse, qrows * 4, "lse")};
-  if ((st = check_alias(ins, 3, outs, 2))) return st;
-  const int bm = tile_m<MODE_CACHE>(D);
+  if ((st = check_alias(ins, 4, outs, 2))) return st;
+  const int bm = sp ? tile_m<MODE_SPARSE>(D) : tile_m<MODE_CACHE>(D);
   const int64_t nqt = (Nq + bm - 1) / bm;
   const int64_t grid = B * Hq * nqt;
   if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
@@ -387,7 +413,19 @@ static int cache_impl(int dtype, const void* q, const void* k, const void* v, vo
   p.ks_b = ks[0];
   p.ks_h = ks[1];
   p.ks_n = ks[2];
-  dispatch_fwd<MODE_CACHE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+  if (sp) {
+    p.win_left = (int)sp->left;
+    p.win_right = (int)sp->right;
+    p.n_global = (int)sp->n_global;
+    p.bmask = sp->mask;
+    p.bm_q = (int)sp->block_q;
+    p.bm_k = (int)sp->block_k;
+    p.bm_nkb = (int)nkb;
+    p.bm_hstride = (sp->mask && sp->mask_heads > 1) ? mbytes / sp->mask_heads : 0;
+    dispatch_fwd<MODE_SPARSE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+  } else {
+    dispatch_fwd<MODE_CACHE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+  }
   return launch_status();
 }
 
@@ -402,6 +440,21 @@ int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void
   ks[1] = Nk * D;
   ks[2] = D;
   return cache_impl(dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, qs, ks, causal, scale, stream);
+}
+
+int sattn_fwd_sparse(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                     int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t win_left,
+                     int64_t win_right, int64_t n_global, const uint8_t* block_mask, int64_t mask_heads,
+                     int64_t block_q, int64_t block_k, float scale, void* stream) {
+  if (Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || D < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  int64_t qs[3], ks[3];
+  if (!product({Hq, Nq, D}, &qs[0]) || !product({Hkv, Nk, D}, &ks[0])) return fail(SATTN_ERR_SHAPE, "size overflow");
+  qs[1] = Nq * D;
+  qs[2] = D;
+  ks[1] = Nk * D;
+  ks[2] = D;
+  const SparseSpec sp{win_left, win_right, n_global, block_mask, mask_heads, block_q, block_k};
+  return cache_impl(dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, qs, ks, causal, scale, stream, &sp);
 }
 
 int sattn_fwd_strided(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,

@@ -171,6 +171,34 @@ int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void
                     int causal, float scale, void* stream);
 
 /*
+ * Sparse attention: sattn_fwd_cache restricted to a sliding window, global
+ * tokens and a block mask ("Attention algorithms and data movement", lesson
+ * 06: count active blocks, block sparsity is a changed operator tested
+ * against the matching sparse reference; lesson 07: window edges and global
+ * tokens united without double-counting). Exact softmax over the kept keys.
+ *
+ *   Shapes, alignment (query i at position p = i + Nk - Nq), GQA map and
+ *   causal rule as in sattn_fwd_cache. Key j is kept for query i iff
+ *     (p - win_left <= j <= p + win_right     -- a bound of -1 is unlimited
+ *      or j < n_global                        -- global keys, seen by all
+ *      or p < n_global)                       -- global queries see all
+ *     and (block_mask is NULL or block_mask[h][i / block_q][j / block_k] != 0)
+ *     and (!causal or j <= p).
+ *   block_mask : device uint8 [mask_heads, ceil(Nq / block_q),
+ *                ceil(Nk / block_k)], mask_heads = 1 (every head) or Hq
+ *                (query head h uses slice h); NULL = no block restriction.
+ *                block_q must be a positive multiple of 32, block_k of 64.
+ *   win_left, win_right >= -1; n_global >= 0. Nk <= 65536.
+ * A query with no kept key is an empty row: O = 0, lse = -inf. Key tiles no
+ * row of a workgroup keeps are neither loaded nor computed.
+ */
+int sattn_fwd_sparse(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal,
+                     int64_t win_left, int64_t win_right, int64_t n_global,
+                     const uint8_t* block_mask, int64_t mask_heads, int64_t block_q, int64_t block_k,
+                     float scale, void* stream);
+
+/*
  * sattn_fwd_cache on strided, sliced, transposed or broadcast read-only
  * inputs, loaded in place ("Intermediate and advanced extension", workshop
  * table, strided-softmax row: address both strides and accept transposed,

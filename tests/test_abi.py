@@ -220,3 +220,21 @@ def test_strided_rejects(lib):
     assert call(qs=None) == "SATTN_ERR_NULL"
     assert call(o=ctypes.c_void_p(0x10000 + 4096)) == "SATTN_ERR_ALIAS"   # o starts inside q (extent 8 KiB)
     assert call(nq=0, q=NULL, k=NULL, v=NULL, o=NULL, lse=NULL) == "SATTN_OK"
+
+
+def test_sparse_rejects(lib):
+    mask = ctypes.c_void_p(0x700000)
+
+    def call(**kw):
+        a = dict(nq=256, nk=256, left=-1, right=-1, g=0, mask=mask, heads=1, bq=64, bk=64, hq=4, o=FAKE4)
+        a.update(kw)
+        return STATUS[lib.sattn_fwd_sparse(1, FAKE, FAKE2, FAKE3, a["o"], FAKE5, 1, a["hq"], 2, a["nq"], a["nk"], 128,
+                                           1, a["left"], a["right"], a["g"], a["mask"], a["heads"], a["bq"],
+                                           a["bk"], F32(0.1), NULL)]
+    assert call(nk=65537, nq=8) == "SATTN_ERR_UNSUPPORTED"       # longer than the tile list
+    assert call(left=-2) == "SATTN_ERR_VALUE"
+    assert call(g=-1) == "SATTN_ERR_VALUE"
+    assert call(bq=48) == "SATTN_ERR_UNSUPPORTED"                # query blocks: multiples of 32
+    assert call(bk=32) == "SATTN_ERR_UNSUPPORTED"                # key blocks: multiples of 64
+    assert call(heads=3) == "SATTN_ERR_SHAPE"                    # 1 or Hq
+    assert call(o=mask) == "SATTN_ERR_ALIAS"                     # output over the mask

@@ -14,7 +14,7 @@ import torch
 import workloads as W
 from exact_tiled_attention_sattn_amd import (sattn_fwd, sattn_fwd_split, sattn_merge, sattn_fwd_varlen,
                                              sattn_fwd_cache, sattn_fwd_split_cache, sattn_fwd_strided,
-                                             SattnError)
+                                             sattn_fwd_sparse, SattnError)
 from oracle import dense
 from tests.parity import check_attention, check_o, check_lse, TOL
 
@@ -621,3 +621,61 @@ def test_strided_inputs(kind, b, hq, hkv, nq, nk, d, dt, causal):
     o2, l2 = sattn_fwd_cache(q.contiguous(), k.contiguous(), v.contiguous(), causal=causal, scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+# ----------------------------------------- sparse: windows, globals, blocks
+SPARSE = [
+    # (B, Hq, Hkv, Nq, Nk, D, dtype, causal, left, right, n_global, mask (heads, bq, bk) or None)
+    (1, 4, 2, 600, 600, 128, "bf16", True, 100, -1, 0, None),       # causal sliding window
+    (1, 2, 2, 700, 700, 64, "fp16", True, 64, -1, 5, None),         # window + global tokens
+    (1, 2, 1, 300, 300, 128, "bf16", False, 40, 40, 3, None),       # band, global queries and keys
+    (2, 4, 4, 512, 512, 128, "bf16", False, -1, -1, 0, (4, 64, 64)),  # per-head block mask
+    (1, 4, 2, 1000, 1000, 64, "fp16", True, 300, -1, 0, (1, 128, 128)),  # shared mask + causal window
+    (1, 2, 1, 200, 900, 128, "bf16", True, 256, -1, 0, None),       # cache alignment, Nq < Nk
+    (1, 2, 2, 333, 333, 32, "fp16", True, 17, 2, 1, (2, 32, 64)),   # small blocks, ragged
+]
+
+
+def _sparse_case(b, hq, hkv, nq, nk, d, dt, mask, seed):
+    q, k, v = W.qkv((b, hq, nq, d), (b, hkv, nk, d), dt, seed)
+    bm = None
+    if mask is not None:
+        heads, bq, bk = mask
+        g = torch.Generator().manual_seed(seed)
+        bm = torch.randint(0, 2, (heads, -(-nq // bq), -(-nk // bk)), generator=g, dtype=torch.uint8)
+        bm[0, 1, :] = 0                   # one query block with no key at all: empty rows
+    return q, k, v, bm
+
+
+@pytest.mark.parametrize("b,hq,hkv,nq,nk,d,dt,causal,left,right,ng,mask", SPARSE)
+def test_sparse_full(b, hq, hkv, nq, nk, d, dt, causal, left, right, ng, mask):
+    _banner("sparse", b, hq, hkv, nq, nk, d, dt, causal, left, right, ng, mask)
+    q, k, v, bm = _sparse_case(b, hq, hkv, nq, nk, d, dt, mask, seed=8000 + nq + d)
+    scale = W.scale_f32(d)
+    bq, bk = (mask[1], mask[2]) if mask else (64, 64)
+    o, lse = sattn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=(left, right), n_global=ng,
+                              block_mask=None if bm is None else bm.to(DEV), block_q=bq, block_k=bk, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.attention_sparse(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal, left, right, ng,
+                                            None if bm is None else bm.numpy()[0] if bm.shape[0] == 1 else bm.numpy(),
+                                            bq, bk)
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "sparse")
+
+
+def test_sparse_keys_outside_the_window_do_not_matter_bitwise():
+    """Causal window of 128 keys: changing key j changes no row whose window
+    does not contain it, bit for bit."""
+    _banner("sparse window perturbation")
+    n, w = 1000, 128
+    q, k, v = (x.to(DEV) for x in W.qkv((1, 2, n, 128), (1, 2, n, 128), "bf16", 8100))
+    o0, l0 = sattn_fwd_sparse(q, k, v, causal=True, window=(w - 1, -1))
+    for j in (0, 300, 640):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, :, j] = 30.0
+        v2[:, :, j] = -500.0
+        o1, l1 = sattn_fwd_sparse(q, k2, v2, causal=True, window=(w - 1, -1))
+        torch.cuda.synchronize()
+        keep = torch.ones(n, dtype=torch.bool)
+        keep[j:j + w] = False                      # rows j .. j+w-1 see key j
+        assert torch.equal(o1[:, :, keep], o0[:, :, keep]) and torch.equal(l1[:, :, keep], l0[:, :, keep]), j
+        assert not torch.equal(o1[:, :, ~keep], o0[:, :, ~keep])

@@ -10,6 +10,9 @@ with the HIP path:
 * ``oracle.dense``  -- numpy float64, the plain dense definition
   O = softmax(scale * Q K^T [+ causal mask]) V with a natural-log logsumexp,
   plus the plain definitions of the split-KV partial states and their merge.
+* ``oracle.backward`` -- numpy float64 gradients (dQ, dK, dV) of the loss
+  sum(dO * O), from the softmax row derivative; grouped KV heads sum their
+  query heads' gradients.
 * ``oracle.online`` -- standard library only (``math``), the mergeable
   (running max m, rescaled exp-sum l, rescaled numerator acc) state with an
   explicit empty identity.

@@ -1,0 +1,64 @@
+"""Float64 gradients of exact softmax attention (numpy). TEST INFRASTRUCTURE ONLY.
+
+For the scalar loss L = sum(dO * O), the vector-Jacobian product of
+O = softmax(S) V with S = scale * Q K^T over the eligible keys, written from
+the softmax row derivative without forming a Jacobian ("Intermediate and
+advanced extension", workshop table, softmax-backward row; "Attention
+algorithms and data movement", lesson 03: differentiate the normalized row,
+probabilities recomputed from the saved normalization state):
+
+    P     = softmax over eligible keys of S (masked entries are 0)
+    dV    = P^T dO
+    dP    = dO V^T
+    dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)          (the softmax row VJP)
+    dQ    = scale * dS K
+    dK    = scale * dS^T Q
+
+An empty row (no eligible key) has P = 0 and contributes nothing. With
+grouped heads (lesson 05, shared gradients) the gradient of a KV head is the
+sum over the query heads that read it, KV head h // (Hq / Hkv).
+"""
+import numpy as np
+
+from oracle.dense import NEG_INF
+
+
+def attention_backward(q, k, v, do, scale, causal=False):
+    """One head, equal lengths (causal: key j eligible for query i iff
+    j <= i). q, k, v, do: [N, D] float64. Returns dq, dk, dv."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    n = q.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] <= np.arange(n)[:, None], s, NEG_INF)
+    m = s.max(axis=1, keepdims=True) if s.size else np.zeros((n, 1))
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m)
+    denom = e.sum(axis=1, keepdims=True)
+    p = np.where(denom > 0, e / np.where(denom > 0, denom, 1.0), 0.0)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward_bhnd(q, k, v, do, scale, causal=False):
+    """q, do: [B, Hq, N, D]; k, v: [B, Hkv, N, D]. Returns dq [B, Hq, N, D]
+    and dk, dv [B, Hkv, N, D], the latter summed over each KV head's query
+    heads in ascending head order."""
+    b_, hq = q.shape[0], q.shape[1]
+    hkv = k.shape[1]
+    group = hq // hkv
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(b_):
+        for h in range(hq):
+            g = h // group
+            a, bk, bv = attention_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            dq[b, h] = a
+            dk[b, g] += bk
+            dv[b, g] += bv
+    return dq, dk, dv

@@ -1,0 +1,94 @@
+"""Pins of the backward oracle (CPU only): torch float64 autograd through
+SDPA, central finite differences, grouped heads against summed expanded
+heads, and closed forms (constant values give zero dQ and dK; the rows of P
+sum to one, so the dV rows sum to the dO rows). The pages ask for exactly
+these references ("Intermediate and advanced workshop validation":
+backward against FP64 autograd and a central finite difference).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import backward, dense
+
+
+def _case(seed, n, d, scale_q=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n, d)) * scale_q
+    k, v, do = (rng.standard_normal((n, d)) for _ in range(3))
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("n,d", [(1, 4), (3, 2), (17, 8), (64, 16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_vs_torch_autograd(n, d, causal):
+    q, k, v, do = _case(n * 10 + d, n, d, 1.5)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = backward.attention_backward(q, k, v, do, scale, causal)
+    qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    o = F.scaled_dot_product_attention(qt[None], kt[None], vt[None], is_causal=causal, scale=scale)[0]
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_central_finite_differences(causal):
+    """d/dx of L = sum(dO * O(q, k, v)) by central differences on every
+    entry, with O from the forward oracle."""
+    q, k, v, do = _case(5, 4, 3, 1.0)
+    dq, dk, dv = backward.attention_backward(q, k, v, do, 0.8, causal)
+    h = 1e-6
+
+    def loss(q_, k_, v_):
+        return float((dense.attention(q_, k_, v_, 0.8, causal)[0] * do).sum())
+    for x, g, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_constant_values_give_zero_query_and_key_gradients():
+    """Every v_j = c: O = c whatever the weights, so dQ = dK = 0; and since
+    each row of P sums to one, sum_j dV_j = sum_i dO_i."""
+    q, k, _, do = _case(6, 20, 5, 2.0)
+    v = np.tile(np.arange(5.0), (20, 1))
+    for causal in (False, True):
+        dq, dk, dv = backward.attention_backward(q, k, v, do, 0.5, causal)
+        assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+        np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_heads_sum_expanded_gradients():
+    rng = np.random.default_rng(7)
+    q, do = (rng.standard_normal((2, 6, 9, 4)) for _ in range(2))
+    k, v = (rng.standard_normal((2, 2, 9, 4)) for _ in range(2))
+    dq, dk, dv = backward.attention_backward_bhnd(q, k, v, do, 0.5, True)
+    qt = torch.from_numpy(q).requires_grad_(True)
+    kt = torch.from_numpy(k).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    o = F.scaled_dot_product_attention(qt, kt.repeat_interleave(3, 1), vt.repeat_interleave(3, 1),
+                                       is_causal=True, scale=0.5)
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_linear_in_output_gradient():
+    q, k, v, do = _case(8, 12, 4)
+    a = backward.attention_backward(q, k, v, do, 0.5, True)
+    b = backward.attention_backward(q, k, v, 3.0 * do, 0.5, True)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(y, 3.0 * x, rtol=1e-12, atol=1e-13)

@@ -252,3 +252,59 @@ def test_online_mutant_is_caught(name, old, new):
     mod = _mutant(oracle.online, old, new)
     results = dict(_online_checks(mod))
     assert not all(results.values()), "mutant '%s' survived every pin: %s" % (name, results)
+
+
+# -------------------------------------------------------- backward battery
+def _backward_checks(bmod):
+    def autograd():
+        rng = np.random.default_rng(9)
+        for causal in (False, True):
+            q, k, v, do = (rng.standard_normal((7, 3)) for _ in range(4))
+            dq, dk, dv = bmod.attention_backward(q * 2, k, v, do, 0.6, causal)
+            qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q * 2, k, v))
+            o = F.scaled_dot_product_attention(qt[None], kt[None], vt[None], is_causal=causal, scale=0.6)[0]
+            o.backward(torch.from_numpy(do))
+            for a, t in ((dq, qt), (dk, kt), (dv, vt)):
+                if not np.allclose(a, t.grad.numpy(), rtol=1e-10, atol=1e-11):
+                    return False
+        return True
+
+    def grouped():
+        rng = np.random.default_rng(10)
+        q, do = (rng.standard_normal((1, 4, 5, 3)) for _ in range(2))
+        k, v = (rng.standard_normal((1, 2, 5, 3)) for _ in range(2))
+        _, dk, _ = bmod.attention_backward_bhnd(q, k, v, do, 0.5, True)
+        want = np.zeros_like(k)
+        for h in range(4):
+            want[0, h // 2] += bmod.attention_backward(q[0, h], k[0, h // 2], v[0, h // 2], do[0, h], 0.5, True)[1]
+        return np.allclose(dk, want, rtol=1e-13, atol=1e-14)
+
+    for name, fn in (("autograd", autograd), ("grouped", grouped)):
+        try:
+            ok = bool(fn())
+        except Exception:
+            ok = False
+        yield name, ok
+
+
+BACKWARD_MUTANTS = [
+    ("softmax row term dropped", "ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp"),
+    ("dK without transpose", "dk = scale * (ds.T @ q)", "dk = scale * (ds @ q)"),
+    ("dQ scale dropped", "dq = scale * (ds @ k)", "dq = (ds @ k)"),
+    ("dV without transpose", "dv = p.T @ do", "dv = p @ do"),
+    ("causal mask dropped in backward", "    if causal:\n        s = np.where(", "    if False:\n        s = np.where("),
+    ("grouped gradients overwritten, not summed", "dk[b, g] += bk", "dk[b, g] = bk"),
+]
+
+
+def test_real_backward_oracle_passes_battery():
+    import oracle.backward
+    assert all(ok for _, ok in _backward_checks(oracle.backward))
+
+
+@pytest.mark.parametrize("name,old,new", BACKWARD_MUTANTS, ids=[m[0] for m in BACKWARD_MUTANTS])
+def test_backward_mutant_is_caught(name, old, new):
+    import oracle.backward
+    mod = _mutant(oracle.backward, old, new)
+    results = dict(_backward_checks(mod))
+    assert not all(results.values()), "mutant '%s' survived every pin: %s" % (name, results)

@@ -410,6 +410,38 @@ def sparse_extra(steps):
     return res
 
 
+def backward_extra(steps):
+    """Backward (dQ, dK, dV) of the batched 4x16x4096x128 bf16 workload,
+    causal and non-causal, on the forward's own O and lse. FLOPs follow the
+    usual convention of five N^2*D products (2.5x the forward: 10*N^2*D per
+    head non-causal, 5*N^2*D causal); the two-kernel schedule here executes
+    seven (S and dP are recomputed by both kernels), also reported."""
+    from exact_tiled_attention_sattn_amd import sattn_fwd, sattn_bwd
+    b, h, n, d = 4, 16, 4096, 128
+    q, k, v = (x.to(DEV) for x in W.qkv((b, h, n, d), (b, h, n, d), "bf16", 3))
+    do = W.randn((b, h, n, d), "bf16", torch.Generator().manual_seed(33)).to(DEV)
+    scale = W.scale_f32(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((b, h, n), dtype=torch.float32, device=DEV)
+    res = {"workload": "backward of batched_4x16x4096x128_bf16",
+           "flop_convention": "10*N^2*D per head noncausal, 5*N^2*D causal (2.5x forward)"}
+    for causal in (False, True):
+        o, lse = sattn_fwd(q, k, v, causal=causal, scale=scale)
+        fn = lambda: sattn_bwd(q, k, v, o, do, lse, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv,  # noqa: E731
+                               delta=delta)
+        fn()
+        torch.cuda.synchronize()
+        assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
+        ms = float(np.mean(time_launches(fn, steps, 2)))
+        fl = 2.5 * dense_flops(b, h, n, d, causal)
+        res["causal" if causal else "noncausal"] = {
+            "ms_mean": ms, "TFLOPs": fl / ms / 1e9, "frac_of_bf16_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "executed_TFLOPs": 3.5 * dense_flops(b, h, n, d, causal) / ms / 1e9}
+    del q, k, v, do, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(budget_s):
     """The FP64 oracle on sampled query rows of the batched workload, both
     variants, on the host cores, scaled to TFLOP/s by the sampled fraction."""
@@ -576,6 +608,8 @@ def main():
         extras["strided_transposed"] = strided_extra(max(3, min(args.steps, 10)))
         log("sparse: window + globals, block mask")
         extras["sparse"] = sparse_extra(max(3, min(args.steps, 10)))
+        log("backward")
+        extras["backward"] = backward_extra(max(3, min(args.steps, 10)))
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -1,0 +1,426 @@
+// Backward pass of exact softmax attention on gfx950 (dQ, dK, dV).
+//
+// For the loss sum(dO * O) with O = softmax(S) V, S = scale * Q K^T:
+//   P = exp(S - lse)            (recomputed from the saved per-row lse)
+//   dV = P^T dO,  dP = dO V^T,  dS = P (dP - Delta),  Delta_i = dO_i . O_i
+//   dQ = scale * dS K,  dK = scale * dS^T Q
+// ("Attention algorithms and data movement", lesson 03: differentiate the
+// normalized row, probabilities recomputed from the saved normalization
+// state; lesson 05: grouped KV heads sum their query heads' gradients.)
+//
+// Two kernels, no atomics, every sum in a fixed order:
+//   bwd_dq_kernel   -- a wave owns 32 queries and walks 64-key K/V tiles
+//                      (the forward's walk); it also forms Delta and stores it.
+//   bwd_dkdv_kernel -- a wave owns 32 keys and walks 64-query Q/dO tiles of
+//                      every query head of its KV head; it runs after the
+//                      dQ kernel on the same stream and reads Delta.
+// MFMA operand layouts follow the forward: a lane owns one row of the 32x32
+// accumulator's columns; operands of the transposed products come from
+// ds_read_b64_tr_b16 on the natural [row][d] LDS layout, in the row order
+// that the packed probabilities imply.
+#pragma once
+
+#include "fwd_kernel.hpp"
+
+namespace sattn {
+
+struct BwdParams {
+  const uint16_t* q;    // [B, Hq, N, D]
+  const uint16_t* k;    // [B, Hkv, N, D]
+  const uint16_t* v;
+  const uint16_t* o;    // [B, Hq, N, D]
+  const uint16_t* dout; // [B, Hq, N, D]
+  const float* lse;     // [B, Hq, N]
+  float* delta;         // [B, Hq, N] workspace: written by the dQ kernel
+  uint16_t* dq;         // [B, Hq, N, D]
+  uint16_t* dk;         // [B, Hkv, N, D]
+  uint16_t* dv;
+  int hq, hkv, n;
+  int nqt;              // dQ kernel: 128-query tiles per head
+  int nkt;              // dK/dV kernel: 128-key tiles per KV head
+  float c;              // scale * log2(e)
+  float scale;
+};
+
+// One 64-row tile of a [row][D] tensor into LDS (swizzled like the forward's
+// K/V tiles): each wave moves its NI 1 KiB pieces.
+template <int D, int NW>
+struct TileLoader {
+  static constexpr int PPR = D / 8;
+  static constexpr int NI = 64 * D * 2 / 1024 / NW;
+  static_assert(NI >= 1 && (64 * D * 2) % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
+  uint32_t voff[NI];
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int slot = (wave * NI + i) * 64 + lane;
+      const int key = slot / PPR;
+      voff[i] = (uint32_t)key * row_bytes + (uint32_t)(((slot % PPR) ^ swz<D>(key)) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, uint32_t soff, uint16_t* dst, int wave_u) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (wave_u * NI + i) * 512),
+                                               16, voff[i], soff, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------- dQ
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
+  constexpr int NW = 4, BM = 128, BN = 64;
+  constexpr int KK = D / 16, KB = BN / 32, DB = D / 32;
+  constexpr int TILE = BN * D;  // elements of one K or V tile
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[2 * TILE];
+
+  // block -> (query head slice, query tile); heads contiguous per XCD,
+  // heaviest (causal: longest) query tiles first
+  const int lin = xcd_linear(blockIdx.x);
+  const int slice = lin / p.nqt;                 // b * Hq + h
+  const int qt = p.nqt - 1 - lin % p.nqt;
+  const int b = slice / p.hq, h = slice % p.hq;
+  const int kvs = b * p.hkv + h / (p.hq / p.hkv);
+  const int q_pos0 = qt * BM;
+  const int nq = min(BM, p.n - q_pos0);
+  const int64_t qbase = ((int64_t)slice * p.n + q_pos0) * D;
+  const int64_t kvbase = (int64_t)kvs * p.n * D;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int qrow = wave * 32 + l32;
+  const bool row_ok = qrow < nq;
+  const int my_pos = q_pos0 + qrow;
+  const bool wave_active = wave * 32 < nq;
+  const int wave_last_pos = q_pos0 + wave * 32 + 31;
+
+  // this lane's query row: Q and dO as MFMA B operands; Delta = dO . O
+  u32x4 qreg[KK], dreg[KK];
+  float delta = 0.f;
+  {
+    const int64_t off = qbase + (int64_t)qrow * D + hf * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qreg[kk] = row_ok ? *(const u32x4*)(p.q + off + kk * 16) : u32x4{0, 0, 0, 0};
+      dreg[kk] = row_ok ? *(const u32x4*)(p.dout + off + kk * 16) : u32x4{0, 0, 0, 0};
+      const u32x4 ov = row_ok ? *(const u32x4*)(p.o + off + kk * 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        delta += E::lo(dreg[kk][j]) * E::lo(ov[j]) + E::hi(dreg[kk][j]) * E::hi(ov[j]);
+    }
+  }
+  delta = sum_halves(delta);
+  const float lse2 = row_ok ? p.lse[(int64_t)slice * p.n + my_pos] * kLog2e : 0.f;
+  if (row_ok && hf == 0) p.delta[(int64_t)slice * p.n + my_pos] = delta;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  const int k_end = CAUSAL ? min(p.n, q_pos0 + BM) : p.n;
+  const int ntiles = (k_end + BN - 1) / BN;
+  const uint32_t row_bytes = (uint32_t)D * 2u;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvbase), (short)0, (int)(k_end * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvbase), (short)0, (int)(k_end * row_bytes), 0x00020000);
+  TileLoader<D, NW> ld;
+  ld.init(wave, lane, row_bytes);
+  auto issue_tile = [&](int t, uint16_t* sb) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(t * BN) * row_bytes);
+    ld.issue(rk, soff, sb, wave_u);
+    ld.issue(rv, soff, sb + TILE, wave_u);
+  };
+
+  int kofs[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) kofs[kk] = l32 * D + (((kk * 2 + hf) ^ swz<D>(l32)) * 8);
+  const int g16 = lane >> 4;
+  const int tr_key = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+  int tofs[2][DB];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = db * 32 + 16 * (g16 & 1) + 4 * (lane & 3);
+      const int key = tr_key + 8 * x;
+      tofs[x][db] = key * D + (((d0 >> 3) ^ swz<D>(key)) * 8) + (d0 & 7);
+    }
+
+  auto step = [&](int t, const uint16_t* cur, uint16_t* nxt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntiles) issue_tile(t + 1, nxt);
+    const int kt0 = t * BN;
+    if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
+    const uint16_t* sK = cur;
+    const uint16_t* sV = cur + TILE;
+    // S^T = K Q^T and dP^T = V dO^T (keys x queries, one query per lane)
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[kb][r] = 0.f;
+        dp[kb][r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s[kb] = E::mfma32(*(const u32x4*)(sK + kofs[kk] + kb * 32 * D), qreg[kk], s[kb]);
+        dp[kb] = E::mfma32(*(const u32x4*)(sV + kofs[kk] + kb * 32 * D), dreg[kk], dp[kb]);
+      }
+    }
+    // P = exp2(S c - lse log2 e) on eligible keys; dS = P (dP - Delta)
+    const bool edge = kt0 + BN > p.n || (CAUSAL && kt0 + BN - 1 > q_pos0 + wave * 32);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = fast_exp2(fmaf(s[kb][r], p.c, -lse2));
+        if (edge) {
+          const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= p.n || (CAUSAL && key > my_pos)) pr = 0.f;
+        }
+        s[kb][r] = pr * (dp[kb][r] - delta);
+      }
+    // dQ^T += K^T dS^T (16 keys per MFMA; K^T by transposing reads)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int o8 = half * 8;
+        const u32x4 pb = {E::pack2(s[kb][o8 + 0], s[kb][o8 + 1]), E::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
+                          E::pack2(s[kb][o8 + 4], s[kb][o8 + 5]), E::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
+        const int krow = (kb * 32 + half * 16) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 a0 = lds_read_tr16(sK + tofs[0][db] + krow);
+          const u32x2 a1 = lds_read_tr16(sK + tofs[1][db] + krow);
+          acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, acc[db]);
+        }
+      }
+  };
+  if (ntiles > 0) {
+    issue_tile(0, sbuf0);
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      step(t, sbuf0, sbuf1);
+      step(t + 1, sbuf1, sbuf0);
+    }
+    if (t < ntiles) step(t, sbuf0, sbuf1);
+  }
+  if (!row_ok) return;
+  uint16_t* op = p.dq + qbase + (int64_t)qrow * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + 8 * g4 + 4 * hf;
+      *(u32x2*)(op + d) = u32x2{E::pack2(acc[db][g4 * 4 + 0] * p.scale, acc[db][g4 * 4 + 1] * p.scale),
+                                E::pack2(acc[db][g4 * 4 + 2] * p.scale, acc[db][g4 * 4 + 3] * p.scale)};
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int NW = 4, BNK = 128, BMQ = 64;
+  constexpr int KK = D / 16, DB = D / 32;
+  constexpr int TILE = BMQ * D;                 // elements of one Q or dO tile
+  constexpr int BUF = 2 * TILE + 2 * BMQ * 2;   // Q, dO, then lse and Delta (fp32)
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[BUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[BUF];
+
+  // block -> (KV slice, key tile); KV heads contiguous per XCD, the keys
+  // that see the most queries (causal: the earliest) first
+  const int lin = xcd_linear(blockIdx.x);
+  const int kvs = lin / p.nkt;                  // b * Hkv + g
+  const int kt = lin % p.nkt;
+  const int b = kvs / p.hkv, g = kvs % p.hkv;
+  const int grp = p.hq / p.hkv;
+  const int k0 = kt * BNK;
+  const int nkeys = min(BNK, p.n - k0);
+  const int64_t kvbase = ((int64_t)kvs * p.n + k0) * D;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int krow = wave * 32 + l32;
+  const bool key_ok = krow < nkeys;
+  const int my_key = k0 + krow;
+  const bool wave_active = wave * 32 < nkeys;
+  const int wave_first_key = k0 + wave * 32;
+
+  // this lane's key: K and V as MFMA B operands (S = Q K^T, dP = dO V^T)
+  u32x4 kreg[KK], vreg[KK];
+  {
+    const int64_t off = kvbase + (int64_t)krow * D + hf * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      kreg[kk] = key_ok ? *(const u32x4*)(p.k + off + kk * 16) : u32x4{0, 0, 0, 0};
+      vreg[kk] = key_ok ? *(const u32x4*)(p.v + off + kk * 16) : u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 adk[DB], adv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      adk[db][r] = 0.f;
+      adv[db][r] = 0.f;
+    }
+
+  // query tiles: every query head of the group, causal from the tile holding k0
+  const int t_begin = CAUSAL ? k0 / BMQ : 0;
+  const int nqt = (p.n + BMQ - 1) / BMQ;
+  const int per_head = nqt - t_begin;
+  const int nsteps = per_head * grp;
+  const uint32_t row_bytes = (uint32_t)D * 2u;
+  TileLoader<D, NW> ld;
+  ld.init(wave, lane, row_bytes);
+  auto issue_step = [&](int it, uint16_t* sb) {
+    const int hh = g * grp + it / per_head;
+    const int t = t_begin + it % per_head;
+    const int64_t slice = (int64_t)b * p.hq + hh;
+    const int q0 = t * BMQ;
+    const int rows = min(BMQ, p.n - q0);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.q + (slice * p.n + q0) * D), (short)0, (int)(rows * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.dout + (slice * p.n + q0) * D), (short)0, (int)(rows * row_bytes), 0x00020000);
+    ld.issue(rq, 0u, sb, wave_u);
+    ld.issue(rd, 0u, sb + TILE, wave_u);
+    if (wave_u == 0) {   // lse and Delta of the tile's rows, 4 bytes per lane
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.lse + slice * p.n + q0), (short)0, rows * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.delta + slice * p.n + q0), (short)0, rows * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(sb + 2 * TILE), 4,
+                                               (uint32_t)lane * 4u, 0u, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + 2 * BMQ),
+                                               4, (uint32_t)lane * 4u, 0u, 0, 0);
+    }
+  };
+
+  int aofs[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) aofs[kk] = l32 * D + (((kk * 2 + hf) ^ swz<D>(l32)) * 8);
+  const int g16 = lane >> 4;
+  const int tr_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+  int tofs[2][DB];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = db * 32 + 16 * (g16 & 1) + 4 * (lane & 3);
+      const int row = tr_row + 8 * x;
+      tofs[x][db] = row * D + (((d0 >> 3) ^ swz<D>(row)) * 8) + (d0 & 7);
+    }
+
+  auto step = [&](int it, const uint16_t* cur, uint16_t* nxt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 < nsteps) issue_step(it + 1, nxt);
+    const int q0 = (t_begin + it % per_head) * BMQ;
+    if (!wave_active) return;
+    const uint16_t* sQ = cur;
+    const uint16_t* sD = cur + TILE;
+    const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
+    const float* sE = sL + BMQ;
+#pragma unroll
+    for (int qb = 0; qb < BMQ / 32; ++qb) {
+      const int qb0 = q0 + qb * 32;
+      if (CAUSAL && qb0 + 31 < wave_first_key) continue;   // every query of the block precedes the wave's keys
+      // S = Q K^T and dP = dO V^T (queries x keys, one key per lane)
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s = E::mfma32(*(const u32x4*)(sQ + aofs[kk] + qb * 32 * D), kreg[kk], s);
+        dp = E::mfma32(*(const u32x4*)(sD + aofs[kk] + qb * 32 * D), vreg[kk], dp);
+      }
+      // register r holds query row qb*32 + 8*(r/4) + 4*hf + r%4
+      f32x4 lse4[4], del4[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        lse4[g4] = *(const f32x4*)(sL + qb * 32 + 8 * g4 + 4 * hf);
+        del4[g4] = *(const f32x4*)(sE + qb * 32 + 8 * g4 + 4 * hf);
+      }
+      const bool edge = qb0 + 32 > p.n || (CAUSAL && qb0 < wave_first_key + 31);
+      f32x16 pr, ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = fast_exp2(fmaf(s[r], p.c, -lse4[r >> 2][r & 3] * kLog2e));
+        if (edge) {
+          const int qi = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (qi >= p.n || (CAUSAL && my_key > qi)) x = 0.f;
+        }
+        pr[r] = x;
+        ds[r] = x * (dp[r] - del4[r >> 2][r & 3]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (16 queries per MFMA)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int o8 = half * 8;
+        const u32x4 pb = {E::pack2(pr[o8 + 0], pr[o8 + 1]), E::pack2(pr[o8 + 2], pr[o8 + 3]),
+                          E::pack2(pr[o8 + 4], pr[o8 + 5]), E::pack2(pr[o8 + 6], pr[o8 + 7])};
+        const u32x4 sb = {E::pack2(ds[o8 + 0], ds[o8 + 1]), E::pack2(ds[o8 + 2], ds[o8 + 3]),
+                          E::pack2(ds[o8 + 4], ds[o8 + 5]), E::pack2(ds[o8 + 6], ds[o8 + 7])};
+        const int qrow = (qb * 32 + half * 16) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 a0 = lds_read_tr16(sD + tofs[0][db] + qrow);
+          const u32x2 a1 = lds_read_tr16(sD + tofs[1][db] + qrow);
+          adv[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, adv[db]);
+          const u32x2 c0 = lds_read_tr16(sQ + tofs[0][db] + qrow);
+          const u32x2 c1 = lds_read_tr16(sQ + tofs[1][db] + qrow);
+          adk[db] = E::mfma32(u32x4{c0[0], c0[1], c1[0], c1[1]}, sb, adk[db]);
+        }
+      }
+    }
+  };
+  if (nsteps > 0) {
+    issue_step(0, sbuf0);
+    int it = 0;
+    for (; it + 1 < nsteps; it += 2) {
+      step(it, sbuf0, sbuf1);
+      step(it + 1, sbuf1, sbuf0);
+    }
+    if (it < nsteps) step(it, sbuf0, sbuf1);
+  }
+  if (!key_ok) return;
+  uint16_t* kp = p.dk + kvbase + (int64_t)krow * D;
+  uint16_t* vp = p.dv + kvbase + (int64_t)krow * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + 8 * g4 + 4 * hf;
+      *(u32x2*)(kp + d) = u32x2{E::pack2(adk[db][g4 * 4 + 0] * p.scale, adk[db][g4 * 4 + 1] * p.scale),
+                                E::pack2(adk[db][g4 * 4 + 2] * p.scale, adk[db][g4 * 4 + 3] * p.scale)};
+      *(u32x2*)(vp + d) = u32x2{E::pack2(adv[db][g4 * 4 + 0], adv[db][g4 * 4 + 1]),
+                                E::pack2(adv[db][g4 * 4 + 2], adv[db][g4 * 4 + 3])};
+    }
+}
+
+// Explicit instantiations: every backward kernel's host stub is emitted
+// here (implicit instantiation through the launches alone left most of them
+// undefined in the shared library).
+#define SATTN_BWD_INST(E_, D_, C_)                                       \
+  template __global__ void bwd_dq_kernel<E_, D_, C_>(const BwdParams); \
+  template __global__ void bwd_dkdv_kernel<E_, D_, C_>(const BwdParams);
+SATTN_BWD_INST(Bf16, 32, false) SATTN_BWD_INST(Bf16, 32, true) SATTN_BWD_INST(Bf16, 64, false)
+SATTN_BWD_INST(Bf16, 64, true) SATTN_BWD_INST(Bf16, 128, false) SATTN_BWD_INST(Bf16, 128, true)
+SATTN_BWD_INST(F16, 32, false) SATTN_BWD_INST(F16, 32, true) SATTN_BWD_INST(F16, 64, false)
+SATTN_BWD_INST(F16, 64, true) SATTN_BWD_INST(F16, 128, false) SATTN_BWD_INST(F16, 128, true)
+#undef SATTN_BWD_INST
+
+}  // namespace sattn

@@ -19,8 +19,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Element traits: the 16-bit storage type, its 32x32x16 MFMA and its
-// round-to-nearest-even packing of two fp32 values.
+// Element traits: the 16-bit storage type, its 32x32x16 MFMA, its
+// round-to-nearest-even packing of two fp32 values and the exact unpacking.
 struct Bf16 {
   static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -32,6 +32,9 @@ struct Bf16 {
     r[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, r);
   }
+  // the two values of a packed word, exactly, as fp32
+  static __device__ __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 };
 
 struct F16 {
@@ -45,6 +48,8 @@ struct F16 {
     r[1] = (_Float16)hi;
     return __builtin_bit_cast(uint32_t, r);
   }
+  static __device__ __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+  static __device__ __forceinline__ float hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

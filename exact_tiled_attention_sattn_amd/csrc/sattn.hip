@@ -12,6 +12,7 @@
 #include "../../include/sattn.h"
 #include "fwd_kernel.hpp"
 #include "fwd_small.hpp"
+#include "bwd_kernel.hpp"
 
 namespace {
 
@@ -145,6 +146,17 @@ void dispatch_split(int dtype, int64_t D, const FwdParams& p, int64_t grid, hipS
     if (D == 32) launch_fwd<F16, 32, CAUSAL, MODE_SPLIT>(p, grid, s);
     else if (D == 64) launch_fwd<F16, 64, CAUSAL, MODE_SPLIT>(p, grid, s);
     else launch_fwd<F16, 128, CAUSAL, MODE_SPLIT>(p, grid, s);
+  }
+}
+
+template <class E, int D>
+void launch_bwd(const BwdParams& p, bool causal, int64_t grid_q, int64_t grid_kv, hipStream_t s) {
+  if (causal) {
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
   }
 }
 
@@ -455,6 +467,63 @@ int sattn_fwd_sparse(int dtype, const void* q, const void* k, const void* v, voi
   ks[2] = D;
   const SparseSpec sp{win_left, win_right, n_global, block_mask, mask_heads, block_q, block_k};
   return cache_impl(dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, qs, ks, causal, scale, stream, &sp);
+}
+
+int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+              int64_t N, int64_t D, int causal, float scale, void* stream) {
+  int st = check_common(dtype, D, scale);
+  if (st) return st;
+  if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return fail(SATTN_ERR_SHAPE, "Hq must be a multiple of Hkv");
+  int64_t qrows, kvrows, qbytes, kvbytes;
+  if (!product({B, Hq, N}, &qrows) || !product({B, Hkv, N}, &kvrows) || !product({qrows, D, 2}, &qbytes) ||
+      !product({kvrows, D, 2}, &kvbytes))
+    return fail(SATTN_ERR_SHAPE, "size overflow");
+  if (qrows == 0) return ok();
+  if (N >= kMaxLen || B * Hq >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "size too large");
+  if (N * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return fail(SATTN_ERR_NULL, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+    return fail(SATTN_ERR_ALIGN, "16-bit tensors need 16-byte, lse/delta 4-byte alignment");
+  Range ins[6] = {range_of(q, qbytes, "q"), range_of(k, kvbytes, "k"), range_of(v, kvbytes, "v"),
+                  range_of(o, qbytes, "o"), range_of(dout, qbytes, "dout"), range_of(lse, qrows * 4, "lse")};
+  Range outs[4] = {range_of(dq, qbytes, "dq"), range_of(dk, kvbytes, "dk"), range_of(dv, kvbytes, "dv"),
+                   range_of(delta, qrows * 4, "delta")};
+  if ((st = check_alias(ins, 6, outs, 4))) return st;
+  BwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)o;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.hq = (int)Hq;
+  p.hkv = (int)Hkv;
+  p.n = (int)N;
+  p.nqt = (int)((N + 127) / 128);
+  p.nkt = (int)((N + 127) / 128);
+  p.c = scale * kLog2e;
+  p.scale = scale;
+  const int64_t grid_q = B * Hq * p.nqt, grid_kv = B * Hkv * p.nkt;
+  if (grid_q >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
+  hipStream_t s = (hipStream_t)stream;
+  // dQ first: it also writes Delta, which the dK/dV kernel reads (stream order)
+  if (dtype == SATTN_BF16) {
+    if (D == 32) launch_bwd<Bf16, 32>(p, causal != 0, grid_q, grid_kv, s);
+    else if (D == 64) launch_bwd<Bf16, 64>(p, causal != 0, grid_q, grid_kv, s);
+    else launch_bwd<Bf16, 128>(p, causal != 0, grid_q, grid_kv, s);
+  } else {
+    if (D == 32) launch_bwd<F16, 32>(p, causal != 0, grid_q, grid_kv, s);
+    else if (D == 64) launch_bwd<F16, 64>(p, causal != 0, grid_q, grid_kv, s);
+    else launch_bwd<F16, 128>(p, causal != 0, grid_q, grid_kv, s);
+  }
+  return launch_status();
 }
 
 int sattn_fwd_strided(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,

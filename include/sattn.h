@@ -171,6 +171,33 @@ int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void
                     int causal, float scale, void* stream);
 
 /*
+ * Backward pass: gradients of the loss sum(dO * O) with respect to q, k, v
+ * ("Attention algorithms and data movement", lesson 03: differentiate the
+ * normalized row with probabilities recomputed from the saved lse; lesson
+ * 05: the query heads sharing a KV head add their gradients into it;
+ * "Intermediate and advanced extension", softmax-backward row: the
+ * vector-Jacobian product without a dense Jacobian).
+ *
+ *   q, o, dout, dq : [B, Hq, N, D];  k, v, dk, dv : [B, Hkv, N, D]  (dtype).
+ *   lse            : [B, Hq, N] float32, as written by sattn_fwd /
+ *                    sattn_fwd_cache for the same q, k, v, causal and scale.
+ *   delta          : [B, Hq, N] float32 workspace (caller-owned, overwritten
+ *                    with rowsum(dout * o); its contents are not a result).
+ *   causal         : nonzero -> key j eligible for query i iff j <= i
+ *                    (equal lengths, as in sattn_fwd).
+ * With P = exp(scale q k^T - lse): dV = P^T dO, dS = P (dO V^T - delta),
+ * dQ = scale dS K, dK = scale dS^T Q, accumulated in fp32 and rounded once;
+ * P and dS enter the matrix products rounded to the input dtype. Two launches
+ * on `stream` (dQ, which also writes delta, then dK/dV); no atomics, so
+ * results are bitwise reproducible. dk, dv of a KV head sum its query heads
+ * in ascending order.
+ */
+int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, float* delta, void* dq, void* dk, void* dv,
+              int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int causal, float scale,
+              void* stream);
+
+/*
  * Sparse attention: sattn_fwd_cache restricted to a sliding window, global
  * tokens and a block mask ("Attention algorithms and data movement", lesson
  * 06: count active blocks, block sparsity is a changed operator tested

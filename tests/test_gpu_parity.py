@@ -14,7 +14,7 @@ import torch
 import workloads as W
 from exact_tiled_attention_sattn_amd import (sattn_fwd, sattn_fwd_split, sattn_merge, sattn_fwd_varlen,
                                              sattn_fwd_cache, sattn_fwd_split_cache, sattn_fwd_strided,
-                                             sattn_fwd_sparse, SattnError)
+                                             sattn_fwd_sparse, sattn_bwd, SattnError)
 from oracle import dense
 from tests.parity import check_attention, check_o, check_lse, TOL
 
@@ -679,3 +679,134 @@ def test_sparse_keys_outside_the_window_do_not_matter_bitwise():
         keep[j:j + w] = False                      # rows j .. j+w-1 see key j
         assert torch.equal(o1[:, :, keep], o0[:, :, keep]) and torch.equal(l1[:, :, keep], l0[:, :, keep]), j
         assert not torch.equal(o1[:, :, ~keep], o0[:, :, ~keep])
+
+
+# ------------------------------------------------------------- backward
+# Tolerance for gradients, derived from the arithmetic (the pages give none).
+# dQ_i = scale * sum_j dS_ij k_j, dK_j = scale * sum_i dS_ij q_i and
+# dV_j = sum_i P_ij dO_i are fp32 sums whose other factor (dS or P) enters the
+# MFMA rounded to the input dtype (unit roundoff u = 2^-8 bf16, 2^-11 fp16);
+# Delta_i = dO_i . O_i uses the output O, itself rounded (|dDelta_i| <=
+# u sum_d |dO_id O_id|), which shifts dS_ij by P_ij dDelta_i; the result is
+# rounded once more. Because sum_j dS_ij = 0 the sums cancel heavily, so the
+# bound is taken on the sums of magnitudes, element by element:
+#   |dq - ref| <= K u (scale (|dS| |K| + dDelta . (P |K|)) + |ref|)   (dk alike)
+#   |dv - ref| <= K u (P^T |dO| + |ref|)
+# with K = 4 for the fp32 accumulation and the rounding of P itself.
+GRAD_U = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+GRAD_K = 4.0
+
+
+def _grad_bounds(q, k, v, do, o, scale, causal):
+    """Per-element bounds (dq, dk, dv) for one head, float64 numpy inputs."""
+    n = q.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], s, -np.inf)
+    pm = np.exp(s - s.max(axis=1, keepdims=True))
+    pm /= pm.sum(axis=1, keepdims=True)
+    dp = do @ v.T
+    ds = pm * (dp - (pm * dp).sum(axis=1, keepdims=True))
+    ddel = (np.abs(do) * np.abs(o)).sum(axis=1, keepdims=True)       # per unit roundoff
+    bq = scale * (np.abs(ds) @ np.abs(k) + ddel * (pm @ np.abs(k)))
+    bk = scale * (np.abs(ds).T @ np.abs(q) + (pm * ddel).T @ np.abs(q))
+    bv = pm.T @ np.abs(do)
+    return bq, bk, bv
+
+
+def _check_grad(g, ref, bound, dtype, what):
+    a = g.detach().cpu().double().numpy()
+    assert np.isfinite(a).all(), what + ": non-finite gradient"
+    u = GRAD_U[dtype]
+    err = np.abs(a - ref)
+    lim = GRAD_K * u * (bound + np.abs(ref)) + 1e-30
+    ratio = float((err / lim).max()) if err.size else 0.0
+    print("[grad] %s max|err| %.3g max bound %.3g worst err/bound %.3f" % (what, float(err.max()),
+                                                                           float(lim.max()), ratio), flush=True)
+    assert ratio <= 1.0, "%s: worst err/bound %.3f" % (what, ratio)
+
+
+def _check_grads(grads, refs, q, k, v, do, o, scale, causal, dtype, what=""):
+    """grads/refs: (dq, dk, dv) for [B, Hq, N, D] / [B, Hkv, N, D]."""
+    qf, kf, vf, dof, of = (W.to_f64(x.cpu()) for x in (q, k, v, do, o))
+    b_, hq, hkv = qf.shape[0], qf.shape[1], kf.shape[1]
+    grp = hq // hkv
+    bq = np.zeros(qf.shape)
+    bk = np.zeros(kf.shape)
+    bv = np.zeros(vf.shape)
+    for b in range(b_):
+        for h in range(hq):
+            g = h // grp
+            x, y, z = _grad_bounds(qf[b, h], kf[b, g], vf[b, g], dof[b, h], of[b, h], scale, causal)
+            bq[b, h] = x
+            bk[b, g] += y
+            bv[b, g] += z
+    for name, g, r, bd in zip(("dq", "dk", "dv"), grads, refs, (bq, bk, bv)):
+        _check_grad(g, r, bd, dtype, what + name)
+
+
+BWD_SMALL = [
+    # (B, Hq, Hkv, N, D, dtype)
+    (1, 1, 1, 1, 32, "fp16"),
+    (1, 2, 2, 64, 64, "bf16"),
+    (1, 2, 1, 100, 128, "bf16"),
+    (2, 4, 2, 300, 64, "fp16"),
+    (1, 3, 3, 257, 128, "bf16"),
+    (1, 8, 2, 513, 128, "fp16"),
+    (1, 2, 2, 200, 32, "bf16"),
+]
+
+
+@pytest.mark.parametrize("b,hq,hkv,n,d,dt", BWD_SMALL)
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_small_full(b, hq, hkv, n, d, dt, causal):
+    _banner("backward", b, hq, hkv, n, d, dt, causal)
+    from oracle import backward
+    seed = 9000 + n + d + hq
+    q, k, v = W.qkv((b, hq, n, d), (b, hkv, n, d), dt, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    do = W.randn((b, hq, n, d), dt, g)
+    scale = W.scale_f32(d)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = sattn_fwd_cache(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = sattn_bwd(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    refs = backward.attention_backward_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), scale, causal)
+    _check_grads((dq, dk, dv), refs, q, k, v, do, o, scale, causal, W.DTYPES[dt])
+
+
+def test_backward_deterministic_and_inputs_preserved():
+    _banner("backward determinism")
+    q, k, v = (x.to(DEV) for x in W.qkv((1, 4, 700, 128), (1, 2, 700, 128), "bf16", 9100))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(DEV)
+    o, lse = sattn_fwd_cache(q, k, v, causal=True)
+    snap = [x.clone() for x in (q, k, v, o, do, lse)]
+    a = sattn_bwd(q, k, v, o, do, lse, causal=True)
+    b_ = sattn_bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b_):
+        assert torch.equal(x, y)
+    for x, y in zip(snap, (q, k, v, o, do, lse)):
+        assert torch.equal(x, y)
+
+
+def test_backward_batched_4x16x4096x128_bf16_two_heads():
+    """The batched workload's shape, causal: two (b, h) slices checked in
+    full against the float64 gradients (every key's dK/dV needs every
+    query, so whole heads are compared)."""
+    _banner("backward 4x16x4096x128 bf16")
+    from oracle import backward
+    b, h, n, d = 4, 16, 4096, 128
+    q, k, v = W.qkv((b, h, n, d), (b, h, n, d), "bf16", 3)
+    do = W.randn((b, h, n, d), "bf16", torch.Generator().manual_seed(33))
+    scale = W.scale_f32(d)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = sattn_fwd(qd, kd, vd, causal=True, scale=scale)
+    dq, dk, dv = sattn_bwd(qd, kd, vd, o, dod, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for (bi, hi) in ((0, 0), (3, 15)):
+        sl = (slice(bi, bi + 1), slice(hi, hi + 1))
+        refs = backward.attention_backward(W.to_f64(q[bi, hi]), W.to_f64(k[bi, hi]), W.to_f64(v[bi, hi]),
+                                           W.to_f64(do[bi, hi]), scale, True)
+        _check_grads((dq[sl], dk[sl], dv[sl]), tuple(r[None, None] for r in refs), q[sl], k[sl], v[sl], do[sl],
+                     o[sl], scale, True, torch.bfloat16, "[%d,%d] " % (bi, hi))

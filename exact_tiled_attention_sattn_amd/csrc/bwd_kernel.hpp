@@ -228,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------- dK, dV
 template <class E, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
+  // queries per step, in 64-row sub-tiles (128 measured no faster)
   constexpr int NW = 4, BNK = 128, BMQ = 64;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int TILE = BMQ * D;                 // elements of one Q or dO tile
@@ -292,17 +293,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
         (void*)(p.q + (slice * p.n + q0) * D), (short)0, (int)(rows * row_bytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.dout + (slice * p.n + q0) * D), (short)0, (int)(rows * row_bytes), 0x00020000);
-    ld.issue(rq, 0u, sb, wave_u);
-    ld.issue(rd, 0u, sb + TILE, wave_u);
+#pragma unroll
+    for (int r = 0; r < BMQ / 64; ++r) {
+      ld.issue(rq, (uint32_t)(r * 64) * row_bytes, sb + r * 64 * D, wave_u);
+      ld.issue(rd, (uint32_t)(r * 64) * row_bytes, sb + TILE + r * 64 * D, wave_u);
+    }
     if (wave_u == 0) {   // lse and Delta of the tile's rows, 4 bytes per lane
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.lse + slice * p.n + q0), (short)0, rows * 4, 0x00020000);
       const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.delta + slice * p.n + q0), (short)0, rows * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(sb + 2 * TILE), 4,
-                                               (uint32_t)lane * 4u, 0u, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + 2 * BMQ),
-                                               4, (uint32_t)lane * 4u, 0u, 0, 0);
+#pragma unroll
+      for (int r = 0; r < BMQ / 64; ++r) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + r * 128),
+                                                 4, (uint32_t)lane * 4u, (uint32_t)r * 256u, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            re, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + 2 * BMQ + r * 128), 4, (uint32_t)lane * 4u,
+            (uint32_t)r * 256u, 0, 0);
+      }
     }
   };
 

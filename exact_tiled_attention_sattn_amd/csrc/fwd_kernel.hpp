@@ -500,6 +500,20 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
 
     if constexpr (FAST) {
       // ---- fixed-reference update: exps against the row's first-tile max
+      if constexpr (SPARSE) {
+        // A row whose first kept key comes after the first tile takes its
+        // reference from the first tile that has one (its acc and l are
+        // still zero, so nothing needs rescaling).
+        if (__builtin_amdgcn_ballot_w64(m == -INFINITY) != 0) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+          mx = max_halves(mx);
+          if (m == -INFINITY) m = mx * c;
+        }
+      }
       const float mref = (EMPTY_ROWS && m == -INFINITY) ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
@@ -641,8 +655,8 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
       else step(t, sbuf0, sbuf1, yes, fast_tag);
     }
   };
-  if constexpr (MODE == MODE_SPLIT || SPARSE) {
-    run(no);  // the partial state exports the exact chunk max; a sparse row's first eligible key can come late
+  if constexpr (MODE == MODE_SPLIT) {
+    run(no);  // the partial state exports the exact chunk max
   } else {
     run(yes);
     if (__syncthreads_or(overflow ? 1 : 0)) {  // rare: redo with the exact update

@@ -810,3 +810,23 @@ def test_backward_batched_4x16x4096x128_bf16_two_heads():
                                            W.to_f64(do[bi, hi]), scale, True)
         _check_grads((dq[sl], dk[sl], dv[sl]), tuple(r[None, None] for r in refs), q[sl], k[sl], v[sl], do[sl],
                      o[sl], scale, True, torch.bfloat16, "[%d,%d] " % (bi, hi))
+
+
+@pytest.mark.parametrize("growth", [3.0, 50.0])
+def test_sparse_late_rows_and_score_growth(growth):
+    """Window of 100 keys with keys growing along the sequence: rows whose
+    first kept key lies after the workgroup's first tile take their reference
+    from the tile that has one; growth 50 makes tile sums overflow the fixed
+    reference, and the workgroup recomputes with the exact update."""
+    _banner("sparse growth", growth)
+    n, d = 700, 128
+    g = torch.Generator().manual_seed(23)
+    q = torch.ones((1, 2, n, d), dtype=torch.bfloat16)
+    k = (torch.linspace(0.0, growth, n)[:, None] * torch.ones(d)).expand(1, 2, n, d).to(torch.bfloat16)
+    v = torch.randn((1, 2, n, d), generator=g).to(torch.bfloat16)
+    scale = W.scale_f32(d)
+    o, lse = sattn_fwd_sparse(q.to(DEV), k.contiguous().to(DEV), v.to(DEV), causal=True, window=(99, -1),
+                              scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.attention_sparse(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, True, 99)
+    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "sparse growth")

@@ -830,3 +830,66 @@ def test_sparse_late_rows_and_score_growth(growth):
     torch.cuda.synchronize()
     o_ref, lse_ref = dense.attention_sparse(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, True, 99)
     check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "sparse growth")
+
+
+# ------------------------------ every entry point: fresh outputs, side stream
+def _nan_like(x):
+    return torch.full_like(x, float("nan"))
+
+
+def test_all_entry_points_fill_nan_outputs_on_a_side_stream_and_preserve_inputs():
+    """Outputs pre-filled with NaN are completely overwritten when each entry
+    point runs on a non-default stream, bit-identical to a default-stream
+    call, and no input changes."""
+    _banner("entry points: fresh outputs / side stream")
+    q, k, v = W.qkv((1, 4, 300, 128), (1, 2, 300, 128), "bf16", 9200)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    qt = q.transpose(1, 2).contiguous().transpose(1, 2)          # strided view of the same values
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16).to(DEV)
+    snap = [x.clone() for x in (q, k, v, do)]
+    cu = torch.tensor([0, 100, 300], dtype=torch.int32, device=DEV)
+    qv, kv, vv = (x[0].transpose(0, 1).contiguous() for x in (q, k, v))   # [T, H, D] packed
+    bm = torch.ones((1, 5, 5), dtype=torch.uint8, device=DEV)
+    o0, l0 = sattn_fwd_cache(q, k, v, causal=True)
+
+    calls = {
+        "cache": lambda o, l: sattn_fwd_cache(q, k, v, causal=True, out=o, lse=l),
+        "strided": lambda o, l: sattn_fwd_strided(qt, k, v, causal=True, out=o, lse=l),
+        "sparse": lambda o, l: sattn_fwd_sparse(q, k, v, causal=True, window=(50, -1), n_global=2, block_mask=bm,
+                                               out=o, lse=l),
+        "varlen": lambda o, l: sattn_fwd_varlen(qv, kv, vv, cu, max_seqlen=200, causal=True, out=o, lse=l),
+    }
+    shapes = {"varlen": (qv, (4, 300))}
+    for name, fn in calls.items():
+        like, lshape = shapes.get(name, (q, (1, 4, 300)))
+        ref_o, ref_l = fn(torch.empty_like(like), torch.empty(lshape, device=DEV))
+        o, l = _nan_like(like), torch.full(lshape, float("nan"), device=DEV)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(o, l)
+        s.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), name
+    # split partials + merge, and the backward, on the side stream
+    pm = torch.full((1, 4, 300, 3), float("nan"), device=DEV)
+    pl, pa = _nan_like(pm), torch.full((1, 4, 300, 3, 128), float("nan"), device=DEV)
+    ref_p = sattn_fwd_split_cache(q, k, v, 128, causal=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sattn_fwd_split_cache(q, k, v, 128, causal=True, part_m=pm, part_l=pl, part_acc=pa)
+        om, lm = sattn_merge(pm, pl, pa, torch.bfloat16, out=_nan_like(q), lse=torch.full((1, 4, 300), float("nan"),
+                                                                                      device=DEV))
+        grads = sattn_bwd(q, k, v, o0, do, l0, causal=True, dq=_nan_like(q), dk=_nan_like(k), dv=_nan_like(v))
+    s.synchronize()
+    torch.cuda.synchronize()
+    for x, y in zip((pm, pl, pa), ref_p):
+        assert torch.equal(x, y)
+    ref_g = sattn_bwd(q, k, v, o0, do, l0, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(grads, ref_g):
+        assert torch.equal(x, y)
+    assert torch.isfinite(om.float()).all() and torch.isfinite(lm).all()
+    for x, y in zip(snap, (q, k, v, do)):
+        assert torch.equal(x, y)

@@ -415,6 +415,36 @@ def test_score_growth_after_first_tile(causal, jump):
     check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "growth")
 
 
+# Many heads at D = 128 (more query tiles than CUs, so a CU runs several
+# workgroups in turn): key-tile counts per query tile even, odd and one;
+# causal pairs with and without a repeated middle tile. Some heads force the
+# exact-update rerun while the other workgroups take the fixed reference.
+# Outputs start as NaN, so every row must be written.
+MANY_HEADS = [(300, 200, False), (300, 150, False), (300, 60, False), (512, 300, True), (1100, 150, True)]
+
+
+@pytest.mark.parametrize("h,n,causal", MANY_HEADS)
+def test_many_heads_with_rerun_heads(h, n, causal):
+    _banner("many heads", h, n, causal)
+    d = 128
+    q, k, v = _dense_inputs(1, h, n, d, "bf16", seed=5000 + h + n)
+    grow = [hh for hh in (3, h // 2, h - 1)] if n > 64 else []
+    for hh in grow:                         # tile sums overflow the fixed reference
+        q[:, hh] = 1.0
+        k[:, hh, :64] = 0.0
+        k[:, hh, 64:] = 50.0
+    scale = W.scale_f32(d)
+    o = torch.full((1, h, n, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((1, h, n), float("nan"), dtype=torch.float32, device=DEV)
+    sattn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    heads = sorted({x for x in (0, 1, 2, 7, 255, 256, 257, h - 2) + tuple(grow) if 0 <= x < h})
+    hs = torch.tensor(heads)
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q[:, hs]), W.to_f64(k[:, hs]), W.to_f64(v[:, hs]), scale, causal)
+    check_attention(o[:, hs.to(DEV)].cpu(), lse[:, hs.to(DEV)].cpu(), o_ref, lse_ref, torch.bfloat16, "many heads")
+
+
 def test_score_growth_varlen_fallback():
     _banner("growth varlen")
     lengths = [200, 130]

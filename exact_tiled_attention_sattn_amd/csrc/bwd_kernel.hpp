@@ -329,6 +329,73 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       tofs[x][db] = row * D + (((d0 >> 3) ^ swz<D>(row)) * 8) + (d0 & 7);
     }
 
+  // Pieces of one 32-query block: S = Q K^T and dP = dO V^T, then
+  // P = exp2(S c - lse log2 e) and dS = P (dP - Delta) packed as MFMA B
+  // operands, then dV^T += dO^T P and dK^T += Q^T dS.
+  auto sd_mfma = [&](const uint16_t* sQ, const uint16_t* sD, int qb, f32x16& s, f32x16& dp) {
+    u32x4 qa[KK], da[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qa[kk] = *(const u32x4*)(sQ + aofs[kk] + qb * 32 * D);
+      da[kk] = *(const u32x4*)(sD + aofs[kk] + qb * 32 * D);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s = E::mfma32(qa[kk], kreg[kk], s);
+      dp = E::mfma32(da[kk], vreg[kk], dp);
+    }
+  };
+  // register r of the 32x32 accumulator holds query row qb*32 + 8*(r/4) +
+  // 4*hf + r%4; `edge` masks queries past N and, causal, before the key
+  auto probs = [&](const float* sL, const float* sE, int qb, const f32x16& s, const f32x16& dp, u32x4 (&pb)[2],
+                   u32x4 (&sb)[2], bool edge, int qb0) {
+    f32x4 lse4[4], del4[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      lse4[g4] = *(const f32x4*)(sL + qb * 32 + 8 * g4 + 4 * hf);
+      del4[g4] = *(const f32x4*)(sE + qb * 32 + 8 * g4 + 4 * hf);
+    }
+    f32x16 pr, ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = fast_exp2(fmaf(s[r], p.c, -lse4[r >> 2][r & 3] * kLog2e));
+      if (edge) {
+        const int qi = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (qi >= p.n || (CAUSAL && my_key > qi)) x = 0.f;
+      }
+      pr[r] = x;
+      ds[r] = x * (dp[r] - del4[r >> 2][r & 3]);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int o8 = half * 8;
+      pb[half] = u32x4{E::pack2(pr[o8 + 0], pr[o8 + 1]), E::pack2(pr[o8 + 2], pr[o8 + 3]),
+                       E::pack2(pr[o8 + 4], pr[o8 + 5]), E::pack2(pr[o8 + 6], pr[o8 + 7])};
+      sb[half] = u32x4{E::pack2(ds[o8 + 0], ds[o8 + 1]), E::pack2(ds[o8 + 2], ds[o8 + 3]),
+                       E::pack2(ds[o8 + 4], ds[o8 + 5]), E::pack2(ds[o8 + 6], ds[o8 + 7])};
+    }
+  };
+  auto dvdk_mfma = [&](const uint16_t* sQ, const uint16_t* sD, int qb, const u32x4 (&pb)[2], const u32x4 (&sb)[2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int qrow = (qb * 32 + half * 16) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 a0 = lds_read_tr16(sD + tofs[0][db] + qrow);
+        const u32x2 a1 = lds_read_tr16(sD + tofs[1][db] + qrow);
+        adv[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[half], adv[db]);
+        const u32x2 c0 = lds_read_tr16(sQ + tofs[0][db] + qrow);
+        const u32x2 c1 = lds_read_tr16(sQ + tofs[1][db] + qrow);
+        adk[db] = E::mfma32(u32x4{c0[0], c0[1], c1[0], c1[1]}, sb[half], adk[db]);
+      }
+    }
+  };
+
   auto step = [&](int it, const uint16_t* cur, uint16_t* nxt) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -339,60 +406,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const uint16_t* sD = cur + TILE;
     const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
     const float* sE = sL + BMQ;
+    // Steps whose queries all exist and all come at or after every key of
+    // the wave need no mask: one branch-free body in which the second
+    // block's S/dP products overlap the first block's exps, and the first
+    // block's dV/dK products the second block's.
+    if (q0 + BMQ <= p.n && (!CAUSAL || q0 >= wave_first_key + 31)) {
+      static_assert(BMQ == 64, "the unmasked body takes two 32-query blocks");
+      f32x16 s0, dp0, s1, dp1;
+      u32x4 pb0[2], sb0[2], pb1[2], sb1[2];
+      sd_mfma(sQ, sD, 0, s0, dp0);
+      __builtin_amdgcn_sched_barrier(0);
+      // The wave issues in order and an MFMA occupies the matrix unit for
+      // several cycles, so VALU work placed between MFMAs runs beside them.
+      sd_mfma(sQ, sD, 1, s1, dp1);
+      probs(sL, sE, 0, s0, dp0, pb0, sb0, false, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);   // operand and lse/Delta reads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk_mfma(sQ, sD, 0, pb0, sb0);
+      probs(sL, sE, 1, s1, dp1, pb1, sb1, false, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk_mfma(sQ, sD, 1, pb1, sb1);
+      return;
+    }
+    // Other steps, block by block: blocks wholly before the wave's keys are
+    // skipped; blocks that straddle them or the query tail are masked.
 #pragma unroll
     for (int qb = 0; qb < BMQ / 32; ++qb) {
       const int qb0 = q0 + qb * 32;
       if (CAUSAL && qb0 + 31 < wave_first_key) continue;   // every query of the block precedes the wave's keys
-      // S = Q K^T and dP = dO V^T (queries x keys, one key per lane)
       f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s = E::mfma32(*(const u32x4*)(sQ + aofs[kk] + qb * 32 * D), kreg[kk], s);
-        dp = E::mfma32(*(const u32x4*)(sD + aofs[kk] + qb * 32 * D), vreg[kk], dp);
-      }
-      // register r holds query row qb*32 + 8*(r/4) + 4*hf + r%4
-      f32x4 lse4[4], del4[4];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        lse4[g4] = *(const f32x4*)(sL + qb * 32 + 8 * g4 + 4 * hf);
-        del4[g4] = *(const f32x4*)(sE + qb * 32 + 8 * g4 + 4 * hf);
-      }
-      const bool edge = qb0 + 32 > p.n || (CAUSAL && qb0 < wave_first_key + 31);
-      f32x16 pr, ds;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = fast_exp2(fmaf(s[r], p.c, -lse4[r >> 2][r & 3] * kLog2e));
-        if (edge) {
-          const int qi = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (qi >= p.n || (CAUSAL && my_key > qi)) x = 0.f;
-        }
-        pr[r] = x;
-        ds[r] = x * (dp[r] - del4[r >> 2][r & 3]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (16 queries per MFMA)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int o8 = half * 8;
-        const u32x4 pb = {E::pack2(pr[o8 + 0], pr[o8 + 1]), E::pack2(pr[o8 + 2], pr[o8 + 3]),
-                          E::pack2(pr[o8 + 4], pr[o8 + 5]), E::pack2(pr[o8 + 6], pr[o8 + 7])};
-        const u32x4 sb = {E::pack2(ds[o8 + 0], ds[o8 + 1]), E::pack2(ds[o8 + 2], ds[o8 + 3]),
-                          E::pack2(ds[o8 + 4], ds[o8 + 5]), E::pack2(ds[o8 + 6], ds[o8 + 7])};
-        const int qrow = (qb * 32 + half * 16) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2 a0 = lds_read_tr16(sD + tofs[0][db] + qrow);
-          const u32x2 a1 = lds_read_tr16(sD + tofs[1][db] + qrow);
-          adv[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, adv[db]);
-          const u32x2 c0 = lds_read_tr16(sQ + tofs[0][db] + qrow);
-          const u32x2 c1 = lds_read_tr16(sQ + tofs[1][db] + qrow);
-          adk[db] = E::mfma32(u32x4{c0[0], c0[1], c1[0], c1[1]}, sb, adk[db]);
-        }
-      }
+      u32x4 pb[2], sb[2];
+      sd_mfma(sQ, sD, qb, s, dp);
+      probs(sL, sE, qb, s, dp, pb, sb, qb0 + 32 > p.n || (CAUSAL && qb0 < wave_first_key + 31), qb0);
+      dvdk_mfma(sQ, sD, qb, pb, sb);
     }
   };
   if (nsteps > 0) {

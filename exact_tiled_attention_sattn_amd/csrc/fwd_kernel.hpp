@@ -364,6 +364,7 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   // rows (packed split rows repeat the Nq positions once per query head).
   const int my_pos = w.pos_mod ? w.q_pos0 + (w.row0 + qrow) % w.pos_mod : w.q_pos0 + qrow;
   const int wave_last_pos = w.pos_mod ? w.q_pos0 + w.pos_mod - 1 : w.q_pos0 + wave * 32 + 31;
+  const int wave_first_pos = w.pos_mod ? w.q_pos0 : w.q_pos0 + wave_u * 32;  // wave-uniform lower bound
   const bool wave_active = wave * 32 < w.nq;
   const float c = p.c;
   const int ntiles = (w.k_end - w.k_begin + BN - 1) / BN;
@@ -474,6 +475,8 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
     // sparse mode also the window / global-token rule, only on listed tiles
     // that some row does not wholly see
     if constexpr (MASKED && !SPARSE) {
+      // only where this wave's rows see a key past the tail or after them
+      if (kt0 + BN > w.k_end || (CAUSAL && kt0 + BN - 1 > wave_first_pos))
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll

@@ -17,7 +17,7 @@ at logical position p iff j <= p, so the diagonal is included ("Logic review
 before implementation": real causal rows include their diagonal). A row with
 no eligible key is the empty row: O = 0, lse = -inf, never NaN (lesson 01 of
 "Attention algorithms and data movement" asks for an explicit empty-row
-contract; the values 0 / -inf are this build's reading).
+contract; the values 0 / -inf are the reading taken here).
 
 All inputs are float64 arrays that already hold the exact values of the stored
 fp16/bf16 tensors; ``scale`` is the float32-rounded scale the GPU receives.
@@ -241,7 +241,7 @@ def sparse_eligibility(nq, nk, causal=False, left=-1, right=-1, n_global=0, bloc
     queries at positions i + (Nk - Nq) (``cache_positions``).
 
     Window and global tokens ("Attention algorithms and data movement",
-    lesson 07; the rule is this build's reading): key j is eligible for the
+    lesson 07; the rule is the reading taken here): key j is eligible for the
     query at position p iff it lies in the window p - left <= j <= p + right
     (a negative bound is unlimited), or j < n_global (a global key, visible
     to every query), or p < n_global (a global query sees every key). The

@@ -21,7 +21,7 @@ follows:
   is handled explicitly, so no NaN can appear.
 * "Attention algorithms and data movement", lesson 01: partials are combined
   with their rescaled denominators, not averaged; the empty row has an
-  explicit result (this build's reading: output 0, logsumexp -inf).
+  explicit result (the reading taken here: output 0, logsumexp -inf).
 """
 import math
 

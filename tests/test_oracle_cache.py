@@ -4,8 +4,8 @@ causal alignment, grouped KV heads, and causal split partial states (CPU).
 The queries are the last Nq tokens of a sequence whose cache holds Nk
 positions, so query i sits at logical position i + (Nk - Nq) ("Attention
 algorithms and data movement", lessons 04 and 05: unequal-length alignment
-and cache payload from logical positions; the rule itself is this build's
-reading). Each test ties ``oracle.dense.attention_cache`` or the causal
+and cache payload from logical positions; the rule itself is the reading
+taken here). Each test ties ``oracle.dense.attention_cache`` or the causal
 ``split_partials`` to something other than itself: brute-force loops, the
 suffix of full self-attention computed by torch's float64 SDPA, torch's SDPA
 with an explicit mask, and closed forms (a single decode query sees every

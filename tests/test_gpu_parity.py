@@ -692,6 +692,28 @@ def test_sparse_full(b, hq, hkv, nq, nk, d, dt, causal, left, right, ng, mask):
     check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "sparse")
 
 
+@pytest.mark.parametrize("causal,masked", [(True, False), (False, True)])
+def test_sparse_longest_tile_list(causal, masked):
+    """Nk = 65536, the longest key range a sparse workgroup can list (1024
+    tiles): the last 160 queries of the cache with every tile kept (causal,
+    no window), or about half of them kept by a random block mask with
+    128-key blocks spread over the whole range."""
+    _banner("sparse longest list", causal, masked)
+    b, hq, hkv, nq, nk, d = 1, 2, 1, 160, 65536, 128
+    q, k, v = W.qkv((b, hq, nq, d), (b, hkv, nk, d), "bf16", 8100 + int(causal))
+    bm = None
+    if masked:
+        g = torch.Generator().manual_seed(8101)
+        bm = torch.randint(0, 2, (hq, -(-nq // 64), nk // 128), generator=g, dtype=torch.uint8)
+    scale = W.scale_f32(d)
+    o, lse = sattn_fwd_sparse(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, n_global=0,
+                              block_mask=None if bm is None else bm.to(DEV), block_q=64, block_k=128, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.attention_sparse(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal, -1, -1, 0,
+                                            None if bm is None else bm.numpy(), 64, 128)
+    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "sparse longest list")
+
+
 def test_sparse_keys_outside_the_window_do_not_matter_bitwise():
     """Causal window of 128 keys: changing key j changes no row whose window
     does not contain it, bit for bit."""

@@ -62,3 +62,31 @@ def attention_backward_bhnd(q, k, v, do, scale, causal=False):
             dk[b, g] += bk
             dv[b, g] += bv
     return dq, dk, dv
+
+
+def attention_backward_varlen(q, k, v, do, cu_seqlens, scale, causal=True):
+    """Packed variable-length grouped-query gradients. q, do: [T, Hq, D];
+    k, v: [T, Hkv, D]; sequence s owns tokens [cu[s], cu[s+1]) and sees only
+    its own keys, causal by position within the sequence ("Attention
+    algorithms and data movement", lesson 04); query head h reads KV head
+    h // (Hq / Hkv), whose gradients sum over its query heads in ascending
+    order (lesson 05). Returns dq [T, Hq, D], dk and dv [T, Hkv, D]; tokens of
+    empty sequences contribute nothing."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    hq, hkv = q.shape[1], k.shape[1]
+    group = hq // hkv
+    cu = [int(x) for x in cu_seqlens]
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if b == a:
+            continue
+        for h in range(hq):
+            g = h // group
+            x, y, z = attention_backward(q[a:b, h], k[a:b, g], v[a:b, g], do[a:b, h], scale, causal)
+            dq[a:b, h] = x
+            dk[a:b, g] += y
+            dv[a:b, g] += z
+    return dq, dk, dv

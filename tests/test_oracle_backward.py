@@ -92,3 +92,32 @@ def test_linear_in_output_gradient():
     b = backward.attention_backward(q, k, v, 3.0 * do, 0.5, True)
     for x, y in zip(a, b):
         np.testing.assert_allclose(y, 3.0 * x, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_vs_autograd_through_packed_mask(causal):
+    """Packed sequences (one of them empty) with grouped heads: torch float64
+    autograd through SDPA over all T tokens with an explicit mask (same
+    sequence, and causal by position within it), on KV heads repeated over
+    their query heads, so autograd itself sums each KV head's gradients."""
+    rng = np.random.default_rng(31)
+    lengths = [5, 0, 9, 1, 7]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    t, hq, hkv, d = int(cu[-1]), 4, 2, 6
+    q, do = rng.standard_normal((t, hq, d)), rng.standard_normal((t, hq, d))
+    k, v = rng.standard_normal((t, hkv, d)), rng.standard_normal((t, hkv, d))
+    scale = 0.45
+    dq, dk, dv = backward.attention_backward_varlen(q, k, v, do, cu, scale, causal)
+    seq = np.repeat(np.arange(len(lengths)), lengths)
+    pos = np.arange(t) - cu[seq]
+    allowed = seq[:, None] == seq[None, :]
+    if causal:
+        allowed &= pos[None, :] <= pos[:, None]
+    qt, kt, vt = (torch.from_numpy(x.transpose(1, 0, 2).copy()).requires_grad_(True) for x in (q, k, v))
+    o = F.scaled_dot_product_attention(qt[None], kt.repeat_interleave(hq // hkv, 0)[None],
+                                       vt.repeat_interleave(hq // hkv, 0)[None],
+                                       attn_mask=torch.from_numpy(allowed), scale=scale)[0]
+    o.backward(torch.from_numpy(do.transpose(1, 0, 2).copy()))
+    np.testing.assert_allclose(dq, qt.grad.numpy().transpose(1, 0, 2), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy().transpose(1, 0, 2), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy().transpose(1, 0, 2), rtol=1e-11, atol=1e-12)

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen", "sattn_fwd_cache",
-    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse", "sattn_bwd",
+    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse", "sattn_bwd", "sattn_bwd_varlen",
     "SattnError", "library", "LIB_PATH", "STATUS",
 ]
 
@@ -73,6 +73,9 @@ def library():
     lib.sattn_bwd.restype = i32
     lib.sattn_bwd.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
                               ctypes.c_float, vp]
+    lib.sattn_bwd_varlen.restype = i32
+    lib.sattn_bwd_varlen.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                     i64, i32, ctypes.c_float, vp]
     lib.sattn_fwd_sparse.restype = i32
     lib.sattn_fwd_sparse.argtypes = [i32, vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64, i32, i64, i64, i64,
                                      vp, i64, i64, i64, ctypes.c_float, vp]
@@ -410,3 +413,55 @@ def sattn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=True, scale=No
                                     _ptr(cu_dev), s, t, int(max_seqlen), hq, hkv, d, int(bool(causal)),
                                     _scale(scale, d), _stream(dev)))
     return out, lse
+
+
+def _cu_device(cu_seqlens, total, max_seqlen, dev):
+    """Host-validated cu_seqlens and its int32 device copy (reused when the
+    caller already passes a contiguous int32 tensor on that device)."""
+    cu_host = cu_seqlens.detach().to("cpu", torch.int64) if isinstance(cu_seqlens, torch.Tensor) else \
+        torch.as_tensor(cu_seqlens, dtype=torch.int64)
+    lengths = (cu_host[1:] - cu_host[:-1]).tolist()
+    if max_seqlen is None:
+        max_seqlen = max(lengths) if lengths else 0
+    check_cu_seqlens(cu_host.tolist(), total, max_seqlen)
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32 \
+            and cu_seqlens.is_contiguous() and cu_seqlens.device == dev:
+        return cu_seqlens, int(max_seqlen)
+    return cu_host.to(torch.int32).to(dev), int(max_seqlen)
+
+
+def sattn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen=None, causal=True, scale=None, dq=None,
+                     dk=None, dv=None, delta=None):
+    """Gradients of sum(dout * o) for o, lse = sattn_fwd_varlen(q, k, v,
+    cu_seqlens). q, o, dout [T,Hq,D]; k, v [T,Hkv,D]; lse [Hq,T] float32;
+    ``delta`` is a float32 [Hq,T] workspace.
+
+    Returns (dq, dk, dv) in q's dtype."""
+    lib = library()
+    _dev_tensor(q, "q", ndim=3)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q must be float16 or bfloat16")
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _dev_tensor(t, name, q.dtype, 3)
+    t_, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (t_, hkv, d) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q/o/dout must be [T,Hq,D] and k/v [T,Hkv,D]")
+    _dev_tensor(lse, "lse", torch.float32, 2)
+    if lse.shape != (hq, t_):
+        raise ValueError("lse must be [Hq, T]")
+    dev = _same_device(q, k, v, o, dout, lse, dq, dk, dv, delta)
+    cu_dev, max_seqlen = _cu_device(cu_seqlens, t_, max_seqlen, dev)
+    dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q.dtype, 3)
+    dk = torch.empty_like(k) if dk is None else _dev_tensor(dk, "dk", q.dtype, 3)
+    dv = torch.empty_like(v) if dv is None else _dev_tensor(dv, "dv", q.dtype, 3)
+    delta = torch.empty((hq, t_), dtype=torch.float32, device=dev) if delta is None else \
+        _dev_tensor(delta, "delta", torch.float32, 2)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape or delta.shape != (hq, t_):
+        raise ValueError("gradient/workspace shape mismatch")
+    with torch.cuda.device(dev):
+        _check(lib.sattn_bwd_varlen(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                    _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_dev),
+                                    cu_dev.numel() - 1, t_, max_seqlen, hq, hkv, d, int(bool(causal)),
+                                    _scale(scale, d), _stream(dev)))
+    return dq, dk, dv

@@ -36,8 +36,13 @@ struct BwdParams {
   uint16_t* dk;         // [B, Hkv, N, D]
   uint16_t* dv;
   int hq, hkv, n;
-  int nqt;              // dQ kernel: 128-query tiles per head
-  int nkt;              // dK/dV kernel: 128-key tiles per KV head
+  int nqt;              // dQ kernel: 128-query tiles per head (varlen: per longest sequence)
+  int nkt;              // dK/dV kernel: 128-key tiles per KV head (varlen: per longest sequence)
+  // varlen: q, o, dout, dq are [T, Hq, D] and k, v, dk, dv [T, Hkv, D]
+  // packed tokens, lse and Delta [Hq, T]; sequence s owns tokens
+  // [cu_seqlens[s], cu_seqlens[s+1]) and positions count from its start
+  const int32_t* cu_seqlens;
+  int nseq, total;
   float c;              // scale * log2(e)
   float scale;
 };
@@ -67,7 +72,7 @@ struct TileLoader {
 };
 
 // ---------------------------------------------------------------- dQ
-template <class E, int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   constexpr int NW = 4, BM = 128, BN = 64;
   constexpr int KK = D / 16, KB = BN / 32, DB = D / 32;
@@ -75,17 +80,50 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[2 * TILE];
 
-  // block -> (query head slice, query tile); heads contiguous per XCD,
-  // heaviest (causal: longest) query tiles first
-  const int lin = xcd_linear(blockIdx.x);
-  const int slice = lin / p.nqt;                 // b * Hq + h
-  const int qt = p.nqt - 1 - lin % p.nqt;
-  const int b = slice / p.hq, h = slice % p.hq;
-  const int kvs = b * p.hkv + h / (p.hq / p.hkv);
-  const int q_pos0 = qt * BM;
-  const int nq = min(BM, p.n - q_pos0);
-  const int64_t qbase = ((int64_t)slice * p.n + q_pos0) * D;
-  const int64_t kvbase = (int64_t)kvs * p.n * D;
+  // block -> (query head, query tile); heaviest (causal: longest) query
+  // tiles first. Dense: heads contiguous per XCD. Varlen: KV head, then
+  // sequence, then query tile, then the query heads of the group, as in the
+  // varlen forward. Offsets in elements: qbase is row q_pos0 of q/o/dout/dq,
+  // kvbase key 0 of k/v, lbase row q_pos0 of lse/Delta.
+  int len, q_pos0;
+  int64_t qbase, kvbase, lbase, q_rs, kv_rs;
+  if constexpr (VARLEN) {
+    const int grp = p.hq / p.hkv;
+    const int lin = xcd_linear(blockIdx.x);
+    const int per_g = p.nseq * p.nqt * grp;
+    const int g = lin / per_g;
+    const int r1 = lin % per_g;
+    const int sq = r1 / (p.nqt * grp);
+    const int r2 = r1 % (p.nqt * grp);
+    const int qt = p.nqt - 1 - r2 / grp;
+    const int h = g * grp + r2 % grp;
+    // clamp the table so that a malformed one cannot address outside [0, T)
+    int a = p.cu_seqlens[sq], e = p.cu_seqlens[sq + 1];
+    a = min(max(a, 0), p.total);
+    e = min(max(e, a), p.total);
+    len = e - a;
+    q_pos0 = qt * BM;
+    if (q_pos0 >= len) return;  // uniform over the workgroup
+    q_rs = (int64_t)p.hq * D;
+    kv_rs = (int64_t)p.hkv * D;
+    qbase = (int64_t)(a + q_pos0) * q_rs + (int64_t)h * D;
+    kvbase = (int64_t)a * kv_rs + (int64_t)g * D;
+    lbase = (int64_t)h * p.total + a + q_pos0;
+  } else {
+    const int lin = xcd_linear(blockIdx.x);
+    const int slice = lin / p.nqt;                 // b * Hq + h
+    const int qt = p.nqt - 1 - lin % p.nqt;
+    const int b = slice / p.hq, h = slice % p.hq;
+    const int kvs = b * p.hkv + h / (p.hq / p.hkv);
+    len = p.n;
+    q_pos0 = qt * BM;
+    q_rs = D;
+    kv_rs = D;
+    qbase = ((int64_t)slice * p.n + q_pos0) * D;
+    kvbase = (int64_t)kvs * p.n * D;
+    lbase = (int64_t)slice * p.n + q_pos0;
+  }
+  const int nq = min(BM, len - q_pos0);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -100,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   u32x4 qreg[KK], dreg[KK];
   float delta = 0.f;
   {
-    const int64_t off = qbase + (int64_t)qrow * D + hf * 8;
+    const int64_t off = qbase + (int64_t)qrow * q_rs + hf * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       qreg[kk] = row_ok ? *(const u32x4*)(p.q + off + kk * 16) : u32x4{0, 0, 0, 0};
@@ -112,8 +150,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     }
   }
   delta = sum_halves(delta);
-  const float lse2 = row_ok ? p.lse[(int64_t)slice * p.n + my_pos] * kLog2e : 0.f;
-  if (row_ok && hf == 0) p.delta[(int64_t)slice * p.n + my_pos] = delta;
+  const float lse2 = row_ok ? p.lse[lbase + qrow] * kLog2e : 0.f;
+  if (row_ok && hf == 0) p.delta[lbase + qrow] = delta;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -121,9 +159,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  const int k_end = CAUSAL ? min(p.n, q_pos0 + BM) : p.n;
+  const int k_end = CAUSAL ? min(len, q_pos0 + BM) : len;
   const int ntiles = (k_end + BN - 1) / BN;
-  const uint32_t row_bytes = (uint32_t)D * 2u;
+  const uint32_t row_bytes = (uint32_t)kv_rs * 2u;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvbase), (short)0, (int)(k_end * row_bytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t rv =
@@ -175,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
       }
     }
     // P = exp2(S c - lse log2 e) on eligible keys; dS = P (dP - Delta)
-    const bool edge = kt0 + BN > p.n || (CAUSAL && kt0 + BN - 1 > q_pos0 + wave * 32);
+    const bool edge = kt0 + BN > len || (CAUSAL && kt0 + BN - 1 > q_pos0 + wave * 32);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -183,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
         float pr = fast_exp2(fmaf(s[kb][r], p.c, -lse2));
         if (edge) {
           const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= p.n || (CAUSAL && key > my_pos)) pr = 0.f;
+          if (key >= len || (CAUSAL && key > my_pos)) pr = 0.f;
         }
         s[kb][r] = pr * (dp[kb][r] - delta);
       }
@@ -214,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     if (t < ntiles) step(t, sbuf0, sbuf1);
   }
   if (!row_ok) return;
-  uint16_t* op = p.dq + qbase + (int64_t)qrow * D;
+  uint16_t* op = p.dq + qbase + (int64_t)qrow * q_rs;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -226,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <class E, int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   // queries per step, in 64-row sub-tiles (128 measured no faster)
   constexpr int NW = 4, BNK = 128, BMQ = 64;
@@ -236,16 +274,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[BUF];
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[BUF];
 
-  // block -> (KV slice, key tile); KV heads contiguous per XCD, the keys
-  // that see the most queries (causal: the earliest) first
-  const int lin = xcd_linear(blockIdx.x);
-  const int kvs = lin / p.nkt;                  // b * Hkv + g
-  const int kt = lin % p.nkt;
-  const int b = kvs / p.hkv, g = kvs % p.hkv;
+  // block -> (KV head, key tile); KV heads contiguous per XCD (varlen: KV
+  // head, then sequence), the keys that see the most queries (causal: the
+  // earliest) first. kvbase is key k0 of k/v/dk/dv in elements; the query
+  // tiles of query head hh start at qhead(hh) in q/dout and at lhead(hh) in
+  // lse/Delta.
   const int grp = p.hq / p.hkv;
-  const int k0 = kt * BNK;
-  const int nkeys = min(BNK, p.n - k0);
-  const int64_t kvbase = ((int64_t)kvs * p.n + k0) * D;
+  int len, k0, g, tok0 = 0, bq = 0;
+  int64_t kvbase, q_rs, kv_rs;
+  if constexpr (VARLEN) {
+    const int lin = xcd_linear(blockIdx.x);
+    const int per_g = p.nseq * p.nkt;
+    g = lin / per_g;
+    const int sq = (lin % per_g) / p.nkt;
+    const int kt = lin % p.nkt;
+    int a = p.cu_seqlens[sq], e = p.cu_seqlens[sq + 1];
+    a = min(max(a, 0), p.total);
+    e = min(max(e, a), p.total);
+    len = e - a;
+    tok0 = a;
+    k0 = kt * BNK;
+    if (k0 >= len) return;  // uniform over the workgroup
+    q_rs = (int64_t)p.hq * D;
+    kv_rs = (int64_t)p.hkv * D;
+    kvbase = (int64_t)(a + k0) * kv_rs + (int64_t)g * D;
+  } else {
+    const int lin = xcd_linear(blockIdx.x);
+    const int kvs = lin / p.nkt;                  // b * Hkv + g
+    const int kt = lin % p.nkt;
+    bq = kvs / p.hkv;
+    g = kvs % p.hkv;
+    len = p.n;
+    k0 = kt * BNK;
+    q_rs = D;
+    kv_rs = D;
+    kvbase = ((int64_t)kvs * p.n + k0) * D;
+  }
+  auto qhead = [&](int hh) -> int64_t {
+    return VARLEN ? (int64_t)tok0 * q_rs + (int64_t)hh * D : ((int64_t)bq * p.hq + hh) * p.n * D;
+  };
+  auto lhead = [&](int hh) -> int64_t {
+    return VARLEN ? (int64_t)hh * p.total + tok0 : ((int64_t)bq * p.hq + hh) * p.n;
+  };
+  const int nkeys = min(BNK, len - k0);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -259,7 +330,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   // this lane's key: K and V as MFMA B operands (S = Q K^T, dP = dO V^T)
   u32x4 kreg[KK], vreg[KK];
   {
-    const int64_t off = kvbase + (int64_t)krow * D + hf * 8;
+    const int64_t off = kvbase + (int64_t)krow * kv_rs + hf * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       kreg[kk] = key_ok ? *(const u32x4*)(p.k + off + kk * 16) : u32x4{0, 0, 0, 0};
@@ -277,22 +348,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 
   // query tiles: every query head of the group, causal from the tile holding k0
   const int t_begin = CAUSAL ? k0 / BMQ : 0;
-  const int nqt = (p.n + BMQ - 1) / BMQ;
+  const int nqt = (len + BMQ - 1) / BMQ;
   const int per_head = nqt - t_begin;
   const int nsteps = per_head * grp;
-  const uint32_t row_bytes = (uint32_t)D * 2u;
+  const uint32_t row_bytes = (uint32_t)q_rs * 2u;
   TileLoader<D, NW> ld;
   ld.init(wave, lane, row_bytes);
   auto issue_step = [&](int it, uint16_t* sb) {
     const int hh = g * grp + it / per_head;
     const int t = t_begin + it % per_head;
-    const int64_t slice = (int64_t)b * p.hq + hh;
     const int q0 = t * BMQ;
-    const int rows = min(BMQ, p.n - q0);
+    const int rows = min(BMQ, len - q0);
+    const int64_t qoff = qhead(hh) + (int64_t)q0 * q_rs;
+    const int64_t loff = lhead(hh) + q0;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.q + (slice * p.n + q0) * D), (short)0, (int)(rows * row_bytes), 0x00020000);
+        (void*)(p.q + qoff), (short)0, (int)(rows * row_bytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.dout + (slice * p.n + q0) * D), (short)0, (int)(rows * row_bytes), 0x00020000);
+        (void*)(p.dout + qoff), (short)0, (int)(rows * row_bytes), 0x00020000);
 #pragma unroll
     for (int r = 0; r < BMQ / 64; ++r) {
       ld.issue(rq, (uint32_t)(r * 64) * row_bytes, sb + r * 64 * D, wave_u);
@@ -300,9 +372,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     }
     if (wave_u == 0) {   // lse and Delta of the tile's rows, 4 bytes per lane
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.lse + slice * p.n + q0), (short)0, rows * 4, 0x00020000);
+          (void*)(p.lse + loff), (short)0, rows * 4, 0x00020000);
       const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.delta + slice * p.n + q0), (short)0, rows * 4, 0x00020000);
+          (void*)(p.delta + loff), (short)0, rows * 4, 0x00020000);
 #pragma unroll
       for (int r = 0; r < BMQ / 64; ++r) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + r * 128),
@@ -366,7 +438,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       float x = fast_exp2(fmaf(s[r], p.c, -lse4[r >> 2][r & 3] * kLog2e));
       if (edge) {
         const int qi = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (qi >= p.n || (CAUSAL && my_key > qi)) x = 0.f;
+        if (qi >= len || (CAUSAL && my_key > qi)) x = 0.f;
       }
       pr[r] = x;
       ds[r] = x * (dp[r] - del4[r >> 2][r & 3]);
@@ -410,7 +482,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // the wave need no mask: one branch-free body in which the second
     // block's S/dP products overlap the first block's exps, and the first
     // block's dV/dK products the second block's.
-    if (q0 + BMQ <= p.n && (!CAUSAL || q0 >= wave_first_key + 31)) {
+    if (q0 + BMQ <= len && (!CAUSAL || q0 >= wave_first_key + 31)) {
       static_assert(BMQ == 64, "the unmasked body takes two 32-query blocks");
       f32x16 s0, dp0, s1, dp1;
       u32x4 pb0[2], sb0[2], pb1[2], sb1[2];
@@ -449,7 +521,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       f32x16 s, dp;
       u32x4 pb[2], sb[2];
       sd_mfma(sQ, sD, qb, s, dp);
-      probs(sL, sE, qb, s, dp, pb, sb, qb0 + 32 > p.n || (CAUSAL && qb0 < wave_first_key + 31), qb0);
+      probs(sL, sE, qb, s, dp, pb, sb, qb0 + 32 > len || (CAUSAL && qb0 < wave_first_key + 31), qb0);
       dvdk_mfma(sQ, sD, qb, pb, sb);
     }
   };
@@ -463,8 +535,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     if (it < nsteps) step(it, sbuf0, sbuf1);
   }
   if (!key_ok) return;
-  uint16_t* kp = p.dk + kvbase + (int64_t)krow * D;
-  uint16_t* vp = p.dv + kvbase + (int64_t)krow * D;
+  uint16_t* kp = p.dk + kvbase + (int64_t)krow * kv_rs;
+  uint16_t* vp = p.dv + kvbase + (int64_t)krow * kv_rs;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -480,13 +552,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 // Explicit instantiations: every backward kernel's host stub is emitted
 // here (implicit instantiation through the launches alone left most of them
 // undefined in the shared library).
-#define SATTN_BWD_INST(E_, D_, C_)                                       \
-  template __global__ void bwd_dq_kernel<E_, D_, C_>(const BwdParams); \
-  template __global__ void bwd_dkdv_kernel<E_, D_, C_>(const BwdParams);
+#define SATTN_BWD_INST2(E_, D_, C_, V_)                                      \
+  template __global__ void bwd_dq_kernel<E_, D_, C_, V_>(const BwdParams); \
+  template __global__ void bwd_dkdv_kernel<E_, D_, C_, V_>(const BwdParams);
+#define SATTN_BWD_INST(E_, D_, C_) SATTN_BWD_INST2(E_, D_, C_, false) SATTN_BWD_INST2(E_, D_, C_, true)
 SATTN_BWD_INST(Bf16, 32, false) SATTN_BWD_INST(Bf16, 32, true) SATTN_BWD_INST(Bf16, 64, false)
 SATTN_BWD_INST(Bf16, 64, true) SATTN_BWD_INST(Bf16, 128, false) SATTN_BWD_INST(Bf16, 128, true)
 SATTN_BWD_INST(F16, 32, false) SATTN_BWD_INST(F16, 32, true) SATTN_BWD_INST(F16, 64, false)
 SATTN_BWD_INST(F16, 64, true) SATTN_BWD_INST(F16, 128, false) SATTN_BWD_INST(F16, 128, true)
 #undef SATTN_BWD_INST
+#undef SATTN_BWD_INST2
 
 }  // namespace sattn

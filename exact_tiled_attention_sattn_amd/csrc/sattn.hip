@@ -149,14 +149,29 @@ void dispatch_split(int dtype, int64_t D, const FwdParams& p, int64_t grid, hipS
   }
 }
 
-template <class E, int D>
+// dQ first: it also writes Delta, which the dK/dV kernel reads (stream order).
+template <class E, int D, bool VARLEN>
 void launch_bwd(const BwdParams& p, bool causal, int64_t grid_q, int64_t grid_kv, hipStream_t s) {
   if (causal) {
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, VARLEN>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, VARLEN>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, VARLEN>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, VARLEN>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+  }
+}
+
+template <bool VARLEN>
+void dispatch_bwd(int dtype, int64_t D, bool causal, const BwdParams& p, int64_t grid_q, int64_t grid_kv,
+                  hipStream_t s) {
+  if (dtype == SATTN_BF16) {
+    if (D == 32) launch_bwd<Bf16, 32, VARLEN>(p, causal, grid_q, grid_kv, s);
+    else if (D == 64) launch_bwd<Bf16, 64, VARLEN>(p, causal, grid_q, grid_kv, s);
+    else launch_bwd<Bf16, 128, VARLEN>(p, causal, grid_q, grid_kv, s);
+  } else {
+    if (D == 32) launch_bwd<F16, 32, VARLEN>(p, causal, grid_q, grid_kv, s);
+    else if (D == 64) launch_bwd<F16, 64, VARLEN>(p, causal, grid_q, grid_kv, s);
+    else launch_bwd<F16, 128, VARLEN>(p, causal, grid_q, grid_kv, s);
   }
 }
 
@@ -512,17 +527,63 @@ int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void
   p.scale = scale;
   const int64_t grid_q = B * Hq * p.nqt, grid_kv = B * Hkv * p.nkt;
   if (grid_q >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
-  hipStream_t s = (hipStream_t)stream;
-  // dQ first: it also writes Delta, which the dK/dV kernel reads (stream order)
-  if (dtype == SATTN_BF16) {
-    if (D == 32) launch_bwd<Bf16, 32>(p, causal != 0, grid_q, grid_kv, s);
-    else if (D == 64) launch_bwd<Bf16, 64>(p, causal != 0, grid_q, grid_kv, s);
-    else launch_bwd<Bf16, 128>(p, causal != 0, grid_q, grid_kv, s);
-  } else {
-    if (D == 32) launch_bwd<F16, 32>(p, causal != 0, grid_q, grid_kv, s);
-    else if (D == 64) launch_bwd<F16, 64>(p, causal != 0, grid_q, grid_kv, s);
-    else launch_bwd<F16, 128>(p, causal != 0, grid_q, grid_kv, s);
-  }
+  dispatch_bwd<false>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
+  return launch_status();
+}
+
+int sattn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* delta, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                     int64_t S, int64_t T, int64_t max_seqlen, int64_t Hq, int64_t Hkv, int64_t D, int causal,
+                     float scale, void* stream) {
+  int st = check_common(dtype, D, scale);
+  if (st) return st;
+  if (S < 0 || T < 0 || max_seqlen < 0 || Hq < 0 || Hkv < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return fail(SATTN_ERR_SHAPE, "Hq must be a multiple of Hkv");
+  int64_t qbytes, kvbytes, lbytes;
+  if (!product({T, Hq, D, 2}, &qbytes) || !product({T, Hkv, D, 2}, &kvbytes) || !product({Hq, T, 4}, &lbytes))
+    return fail(SATTN_ERR_SHAPE, "size overflow");
+  if (S == 0 || T == 0 || Hq == 0 || max_seqlen == 0) return ok();
+  if (T >= kMaxLen || S >= kMaxLen || Hq >= 65536 || max_seqlen > T)
+    return fail(max_seqlen > T ? SATTN_ERR_SHAPE : SATTN_ERR_UNSUPPORTED, "max_seqlen > T or size too large");
+  if (max_seqlen * Hkv * D * 2 >= kMaxSpan || 64 * Hq * D * 2 >= kMaxSpan)
+    return fail(SATTN_ERR_UNSUPPORTED, "a sequence's K/V span exceeds 2 GiB");
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv || !cu_seqlens)
+    return fail(SATTN_ERR_NULL, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4) ||
+      !aligned(cu_seqlens, 4))
+    return fail(SATTN_ERR_ALIGN, "16-bit tensors need 16-byte, lse/delta/cu_seqlens 4-byte alignment");
+  Range ins[7] = {range_of(q, qbytes, "q"),       range_of(k, kvbytes, "k"),        range_of(v, kvbytes, "v"),
+                  range_of(o, qbytes, "o"),       range_of(dout, qbytes, "dout"),   range_of(lse, lbytes, "lse"),
+                  range_of(cu_seqlens, (S + 1) * 4, "cu_seqlens")};
+  Range outs[4] = {range_of(dq, qbytes, "dq"), range_of(dk, kvbytes, "dk"), range_of(dv, kvbytes, "dv"),
+                   range_of(delta, lbytes, "delta")};
+  if ((st = check_alias(ins, 7, outs, 4))) return st;
+  const int64_t ntile = (max_seqlen + 127) / 128;
+  int64_t grid_q, grid_kv;
+  if (!product({S, ntile, Hq}, &grid_q) || !product({S, ntile, Hkv}, &grid_kv) || grid_q >= (int64_t(1) << 31))
+    return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
+  BwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)o;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.hq = (int)Hq;
+  p.hkv = (int)Hkv;
+  p.nqt = (int)ntile;
+  p.nkt = (int)ntile;
+  p.cu_seqlens = cu_seqlens;
+  p.nseq = (int)S;
+  p.total = (int)T;
+  p.c = scale * kLog2e;
+  p.scale = scale;
+  dispatch_bwd<true>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
   return launch_status();
 }
 

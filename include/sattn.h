@@ -198,6 +198,33 @@ int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void
               void* stream);
 
 /*
+ * Backward pass of sattn_fwd_varlen: the same gradients as sattn_bwd for
+ * packed variable-length sequences with grouped KV heads ("Attention
+ * algorithms and data movement", lesson 04: per-sequence boundaries and
+ * positions; lesson 05: shared KV-head gradients).
+ *
+ *   q, o, dout, dq : [T, Hq, D];  k, v, dk, dv : [T, Hkv, D]  (dtype).
+ *   lse            : [Hq, T] float32, as written by sattn_fwd_varlen for the
+ *                    same inputs, cu_seqlens, causal and scale.
+ *   delta          : [Hq, T] float32 workspace (caller-owned, overwritten).
+ *   cu_seqlens     : device int32 [S+1], the same table as the forward
+ *                    (cu[0] = 0, non-decreasing, cu[S] = T, every length
+ *                    <= max_seqlen); validated on a host copy by the caller,
+ *                    clamped to [0, T] by the kernels.
+ *   causal         : nonzero -> key j eligible for query i of the same
+ *                    sequence iff j <= i (positions within the sequence).
+ * Tokens of a sequence see only that sequence. Every token row of dq, dk, dv
+ * that belongs to a sequence is written; dk, dv of a KV head sum its query
+ * heads in ascending order. Two launches on `stream`, no atomics.
+ * Errors as sattn_fwd_varlen, plus null or misaligned gradient buffers and
+ * overlaps of any output with any input.
+ */
+int sattn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* delta, void* dq, void* dk, void* dv, const int32_t* cu_seqlens,
+                     int64_t S, int64_t T, int64_t max_seqlen, int64_t Hq, int64_t Hkv, int64_t D, int causal,
+                     float scale, void* stream);
+
+/*
  * Sparse attention: sattn_fwd_cache restricted to a sliding window, global
  * tokens and a block mask ("Attention algorithms and data movement", lesson
  * 06: count active blocks, block sparsity is a changed operator tested

@@ -238,3 +238,71 @@ def test_sparse_rejects(lib):
     assert call(bk=32) == "SATTN_ERR_UNSUPPORTED"                # key blocks: multiples of 64
     assert call(heads=3) == "SATTN_ERR_SHAPE"                    # 1 or Hq
     assert call(o=mask) == "SATTN_ERR_ALIAS"                     # output over the mask
+
+
+# Backward entry points: q 0x100000, k 0x200000, v 0x300000, o 0x400000,
+# dout 0x500000, lse 0x600000, delta 0x700000, dq 0x800000, dk 0x900000,
+# dv 0xA00000, cu_seqlens 0xB00000 (each 1 MiB apart; the buffers below are
+# a few KiB).
+def _bp(x):
+    return ctypes.c_void_p(x)
+
+
+BWD_PTRS = dict(q=0x100000, k=0x200000, v=0x300000, o=0x400000, dout=0x500000, lse=0x600000, delta=0x700000,
+                dq=0x800000, dk=0x900000, dv=0xA00000)
+
+
+def _bwd(lib, dtype=1, b=1, hq=2, hkv=1, n=8, d=64, **ptrs):
+    a = dict(BWD_PTRS)
+    a.update(ptrs)
+    return lib.sattn_bwd(dtype, *(_bp(a[x]) for x in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv")),
+                         b, hq, hkv, n, d, 1, F32(0.125), NULL)
+
+
+def _bwd_varlen(lib, dtype=1, s=2, t=8, max_seqlen=5, hq=2, hkv=1, d=64, cu=0xB00000, **ptrs):
+    a = dict(BWD_PTRS)
+    a.update(ptrs)
+    return lib.sattn_bwd_varlen(dtype, *(_bp(a[x]) for x in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk",
+                                                              "dv")),
+                                _bp(cu), s, t, max_seqlen, hq, hkv, d, 1, F32(0.125), NULL)
+
+
+BWD_REJECTS = [
+    (dict(dtype=5), "SATTN_ERR_DTYPE"),
+    (dict(d=48), "SATTN_ERR_UNSUPPORTED"),
+    (dict(hq=3, hkv=2), "SATTN_ERR_SHAPE"),
+    (dict(dq=0), "SATTN_ERR_NULL"),
+    (dict(delta=0), "SATTN_ERR_NULL"),
+    (dict(dq=0x800008), "SATTN_ERR_ALIGN"),
+    (dict(delta=0x700002), "SATTN_ERR_ALIGN"),
+    (dict(dq=0x100000), "SATTN_ERR_ALIAS"),          # dq over q
+    (dict(dk=0x200000 + 256), "SATTN_ERR_ALIAS"),    # dk inside k
+    (dict(dv=0x900000), "SATTN_ERR_ALIAS"),          # dv over dk (two outputs)
+    (dict(delta=0x600000), "SATTN_ERR_ALIAS"),       # delta over lse
+]
+
+
+@pytest.mark.parametrize("kwargs,status", BWD_REJECTS + [(dict(n=-1), "SATTN_ERR_SHAPE")])
+def test_bwd_rejects(lib, kwargs, status):
+    st = _bwd(lib, **kwargs)
+    assert STATUS[st] == status, (STATUS[st], lib.sattn_last_error())
+
+
+@pytest.mark.parametrize("kwargs,status", BWD_REJECTS + [
+    (dict(s=-1), "SATTN_ERR_SHAPE"),
+    (dict(max_seqlen=9), "SATTN_ERR_SHAPE"),          # longer than T
+    (dict(cu=0), "SATTN_ERR_NULL"),
+    (dict(cu=0xB00002), "SATTN_ERR_ALIGN"),
+    (dict(delta=0xB00000), "SATTN_ERR_ALIAS"),        # delta over cu_seqlens
+])
+def test_bwd_varlen_rejects(lib, kwargs, status):
+    st = _bwd_varlen(lib, **kwargs)
+    assert STATUS[st] == status, (STATUS[st], lib.sattn_last_error())
+
+
+def test_bwd_zero_sizes_ok_without_pointers(lib):
+    nulls = {x: 0 for x in BWD_PTRS}
+    assert _bwd(lib, n=0, **nulls) == 0
+    assert _bwd(lib, b=0, **nulls) == 0
+    assert _bwd_varlen(lib, t=0, s=0, max_seqlen=0, cu=0, **nulls) == 0
+    assert _bwd_varlen(lib, s=0, cu=0, **nulls) == 0

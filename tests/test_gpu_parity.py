@@ -14,7 +14,7 @@ import torch
 import workloads as W
 from exact_tiled_attention_sattn_amd import (sattn_fwd, sattn_fwd_split, sattn_merge, sattn_fwd_varlen,
                                              sattn_fwd_cache, sattn_fwd_split_cache, sattn_fwd_strided,
-                                             sattn_fwd_sparse, sattn_bwd, SattnError)
+                                             sattn_fwd_sparse, sattn_bwd, sattn_bwd_varlen, SattnError)
 from oracle import dense
 from tests.parity import check_attention, check_o, check_lse, TOL
 
@@ -746,15 +746,23 @@ def test_sparse_keys_outside_the_window_do_not_matter_bitwise():
 #   |dv - ref| <= K u (P^T |dO| + |ref|)
 # with K = 4 for the fp32 accumulation and the rounding of P itself.
 GRAD_U = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+# absolute rounding error of a value below the dtype's normal range (half the
+# subnormal spacing): fp16 P and dS values under 2^-14 round to multiples of
+# 2^-24; bf16 shares fp32's exponent range, where this never matters here
+GRAD_ETA = {torch.bfloat16: 2.0 ** -134, torch.float16: 2.0 ** -25}
 GRAD_K = 4.0
 
 
 def _grad_bounds(q, k, v, do, o, scale, causal):
-    """Per-element bounds (dq, dk, dv) for one head, float64 numpy inputs."""
+    """Per-element bounds for one head, float64 numpy inputs: the relative
+    part (dq, dk, dv), in units of u, and the underflow part (dq, dk, dv), in
+    units of the absolute error of one rounded P or dS element."""
     n = q.shape[0]
     s = scale * (q @ k.T)
+    elig = np.ones((n, n))
     if causal:
-        s = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], s, -np.inf)
+        elig = (np.arange(n)[None, :] <= np.arange(n)[:, None]).astype(np.float64)
+        s = np.where(elig > 0, s, -np.inf)
     pm = np.exp(s - s.max(axis=1, keepdims=True))
     pm /= pm.sum(axis=1, keepdims=True)
     dp = do @ v.T
@@ -763,15 +771,20 @@ def _grad_bounds(q, k, v, do, o, scale, causal):
     bq = scale * (np.abs(ds) @ np.abs(k) + ddel * (pm @ np.abs(k)))
     bk = scale * (np.abs(ds).T @ np.abs(q) + (pm * ddel).T @ np.abs(q))
     bv = pm.T @ np.abs(do)
-    return bq, bk, bv
+    aq = scale * (elig @ np.abs(k))          # dS_ij rounded, times |K_j|
+    ak = scale * (elig.T @ np.abs(q))
+    av = elig.T @ np.abs(do)                  # P_ij rounded, times |dO_i|
+    return (bq, bk, bv), (aq, ak, av)
 
 
-def _check_grad(g, ref, bound, dtype, what):
+def _check_grad(g, ref, bound, abound, dtype, what):
     a = g.detach().cpu().double().numpy()
     assert np.isfinite(a).all(), what + ": non-finite gradient"
     u = GRAD_U[dtype]
     err = np.abs(a - ref)
-    lim = GRAD_K * u * (bound + np.abs(ref)) + 1e-30
+    # relative rounding, plus the absolute floor below the normal range: of
+    # the rounded P / dS operands (abound) and of the stored gradient (1)
+    lim = GRAD_K * (u * (bound + np.abs(ref)) + GRAD_ETA[dtype] * (abound + 1.0)) + 1e-30
     ratio = float((err / lim).max()) if err.size else 0.0
     print("[grad] %s max|err| %.3g max bound %.3g worst err/bound %.3f" % (what, float(err.max()),
                                                                            float(lim.max()), ratio), flush=True)
@@ -783,18 +796,18 @@ def _check_grads(grads, refs, q, k, v, do, o, scale, causal, dtype, what=""):
     qf, kf, vf, dof, of = (W.to_f64(x.cpu()) for x in (q, k, v, do, o))
     b_, hq, hkv = qf.shape[0], qf.shape[1], kf.shape[1]
     grp = hq // hkv
-    bq = np.zeros(qf.shape)
-    bk = np.zeros(kf.shape)
-    bv = np.zeros(vf.shape)
+    rel = [np.zeros(x.shape) for x in (qf, kf, vf)]
+    und = [np.zeros(x.shape) for x in (qf, kf, vf)]
     for b in range(b_):
         for h in range(hq):
             g = h // grp
-            x, y, z = _grad_bounds(qf[b, h], kf[b, g], vf[b, g], dof[b, h], of[b, h], scale, causal)
-            bq[b, h] = x
-            bk[b, g] += y
-            bv[b, g] += z
-    for name, g, r, bd in zip(("dq", "dk", "dv"), grads, refs, (bq, bk, bv)):
-        _check_grad(g, r, bd, dtype, what + name)
+            r3, a3 = _grad_bounds(qf[b, h], kf[b, g], vf[b, g], dof[b, h], of[b, h], scale, causal)
+            for dst, src in ((rel, r3), (und, a3)):
+                dst[0][b, h] = src[0]
+                dst[1][b, g] += src[1]
+                dst[2][b, g] += src[2]
+    for i, (name, g, r) in enumerate(zip(("dq", "dk", "dv"), grads, refs)):
+        _check_grad(g, r, rel[i], und[i], dtype, what + name)
 
 
 BWD_SMALL = [
@@ -825,6 +838,100 @@ def test_backward_small_full(b, hq, hkv, n, d, dt, causal):
     torch.cuda.synchronize()
     refs = backward.attention_backward_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), scale, causal)
     _check_grads((dq, dk, dv), refs, q, k, v, do, o, scale, causal, W.DTYPES[dt])
+
+
+def _check_grads_varlen(grads, refs, q, k, v, do, o, cu, scale, causal, dtype, what="varlen "):
+    """grads/refs: (dq, dk, dv) for [T, Hq, D] / [T, Hkv, D] packed tokens;
+    per-element bounds from each (sequence, head) slice."""
+    qf, kf, vf, dof, of = (W.to_f64(x.cpu()) for x in (q, k, v, do, o))
+    hq, hkv = qf.shape[1], kf.shape[1]
+    grp = hq // hkv
+    rel = [np.zeros(x.shape) for x in (qf, kf, vf)]
+    und = [np.zeros(x.shape) for x in (qf, kf, vf)]
+    for a, e in zip(cu[:-1], cu[1:]):
+        if e == a:
+            continue
+        for h in range(hq):
+            g = h // grp
+            r3, a3 = _grad_bounds(qf[a:e, h], kf[a:e, g], vf[a:e, g], dof[a:e, h], of[a:e, h], scale, causal)
+            for dst, src in ((rel, r3), (und, a3)):
+                dst[0][a:e, h] = src[0]
+                dst[1][a:e, g] += src[1]
+                dst[2][a:e, g] += src[2]
+    for i, (name, g, r) in enumerate(zip(("dq", "dk", "dv"), grads, refs)):
+        _check_grad(g, r, rel[i], und[i], dtype, what + name)
+
+
+BWD_VARLEN = [
+    # (lengths, Hq, Hkv, D, dtype)
+    ([5, 0, 130, 1, 64], 4, 2, 128, "bf16"),       # an empty sequence, single tokens, tile edges
+    ([300, 257], 2, 2, 64, "fp16"),
+    ([200, 0, 77, 129], 8, 2, 32, "bf16"),
+    ([513], 4, 1, 128, "fp16"),
+]
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,d,dt", BWD_VARLEN)
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_varlen_full(lengths, hq, hkv, d, dt, causal):
+    _banner("backward varlen", lengths, hq, hkv, d, dt, causal)
+    from oracle import backward
+    t = sum(lengths)
+    cu = W.cu_seqlens_of(lengths)
+    seed = 9300 + t + d + hq
+    q, k, v = W.qkv((t, hq, d), (t, hkv, d), dt, seed)
+    do = W.randn((t, hq, d), dt, torch.Generator().manual_seed(seed + 1))
+    scale = W.scale_f32(d)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    cud = torch.from_numpy(cu).to(DEV)
+    o, lse = sattn_fwd_varlen(qd, kd, vd, cud, causal=causal, scale=scale)
+    nan = float("nan")
+    dq, dk, dv = (torch.full_like(x, nan) for x in (qd, kd, vd))
+    sattn_bwd_varlen(qd, kd, vd, o, dod, lse, cud, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    refs = backward.attention_backward_varlen(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), cu, scale,
+                                              causal)
+    _check_grads_varlen((dq, dk, dv), refs, q, k, v, do, o, [int(x) for x in cu], scale, causal, W.DTYPES[dt])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_varlen_one_sequence_is_dense_bitwise(causal):
+    """One packed sequence of length N is the dense [1, H, N, D] problem:
+    same tiles, same sums in the same order, so the same bits."""
+    _banner("backward varlen == dense", causal)
+    n, hq, hkv, d = 777, 4, 2, 128
+    q, k, v = (x.to(DEV) for x in W.qkv((n, hq, d), (n, hkv, d), "bf16", 9400))
+    do = W.randn((n, hq, d), "bf16", torch.Generator().manual_seed(9401)).to(DEV)
+    cu = torch.tensor([0, n], dtype=torch.int32, device=DEV)
+    o, lse = sattn_fwd_varlen(q, k, v, cu, causal=causal)
+    got = sattn_bwd_varlen(q, k, v, o, do, lse, cu, causal=causal)
+    bh = lambda x: x.permute(1, 0, 2).unsqueeze(0).contiguous()      # [T, H, D] -> [1, H, T, D]
+    want = sattn_bwd(bh(q), bh(k), bh(v), bh(o), bh(do), lse.unsqueeze(0).contiguous(), causal=causal)
+    torch.cuda.synchronize()
+    for g, w in zip(got, want):
+        assert torch.equal(bh(g), w)
+
+
+def test_backward_varlen_sequences_are_isolated_bitwise():
+    """Changing every token of one sequence leaves the other sequences'
+    gradients bit-identical."""
+    _banner("backward varlen isolation")
+    lengths = [300, 450, 200]
+    t = sum(lengths)
+    cu = torch.from_numpy(W.cu_seqlens_of(lengths)).to(DEV)
+    q, k, v = (x.to(DEV) for x in W.qkv((t, 4, 64), (t, 2, 64), "fp16", 9500))
+    do = W.randn((t, 4, 64), "fp16", torch.Generator().manual_seed(9501)).to(DEV)
+    o, lse = sattn_fwd_varlen(q, k, v, cu)
+    a = sattn_bwd_varlen(q, k, v, o, do, lse, cu)
+    q2, k2, v2, do2 = (x.clone() for x in (q, k, v, do))
+    for x in (q2, k2, v2, do2):
+        x[300:750] = -x[300:750] * 0.5
+    o2, lse2 = sattn_fwd_varlen(q2, k2, v2, cu)
+    b_ = sattn_bwd_varlen(q2, k2, v2, o2, do2, lse2, cu)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b_):
+        assert torch.equal(x[:300], y[:300]) and torch.equal(x[750:], y[750:])
+        assert not torch.equal(x[300:750], y[300:750])
 
 
 def test_backward_deterministic_and_inputs_preserved():

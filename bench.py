@@ -442,6 +442,38 @@ def backward_extra(steps):
     return res
 
 
+def varlen_backward_extra(steps):
+    """Backward of the packed varlen GQA workload (8 seeded sequence lengths,
+    32 query heads on 8 KV heads, D = 128, bf16, causal) on the forward's own
+    O and lse. FLOPs: 2.5x the forward's causal count, as for the batched
+    backward."""
+    from exact_tiled_attention_sattn_amd import sattn_fwd_varlen, sattn_bwd_varlen
+    cfg = W.WORKLOADS["varlen_gqa_8seq_32q8kv_128_bf16_causal"]
+    lengths = W.varlen_lengths(cfg["seed"], cfg["S"], cfg["max_len"])
+    hq, hkv, d = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    t = int(lengths.sum())
+    q, k, v = (x.to(DEV) for x in W.qkv((t, hq, d), (t, hkv, d), "bf16", cfg["seed"]))
+    do = W.randn((t, hq, d), "bf16", torch.Generator().manual_seed(cfg["seed"] + 1)).to(DEV)
+    cu = torch.from_numpy(W.cu_seqlens_of(lengths)).to(DEV)
+    mx = int(lengths.max())
+    scale = W.scale_f32(d)
+    o, lse = sattn_fwd_varlen(q, k, v, cu, max_seqlen=mx, causal=True, scale=scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((hq, t), dtype=torch.float32, device=DEV)
+    fn = lambda: sattn_bwd_varlen(q, k, v, o, do, lse, cu, max_seqlen=mx, causal=True, scale=scale,  # noqa: E731
+                                  dq=dq, dk=dk, dv=dv, delta=delta)
+    fn()
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
+    ms = float(np.mean(time_launches(fn, steps, 2)))
+    flops = 2.5 * sum(2 * int(L) * int(L) * d * hq for L in lengths)
+    del q, k, v, do, dq, dk, dv, o
+    torch.cuda.empty_cache()
+    return {"workload": "backward of varlen_gqa_8seq_32q8kv_128_bf16_causal", "T": t, "ms_mean": ms,
+            "TFLOPs": flops / ms / 1e9, "frac_of_bf16_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "flop_convention": "2.5x the forward's causal 2*L^2*D per query head"}
+
+
 def cpu_baseline(budget_s):
     """The FP64 oracle on sampled query rows of the batched workload, both
     variants, on the host cores, scaled to TFLOP/s by the sampled fraction."""
@@ -610,6 +642,8 @@ def main():
         extras["sparse"] = sparse_extra(max(3, min(args.steps, 10)))
         log("backward")
         extras["backward"] = backward_extra(max(3, min(args.steps, 10)))
+        log("backward: packed varlen GQA")
+        extras["varlen_backward"] = varlen_backward_extra(max(3, min(args.steps, 10)))
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -279,7 +279,24 @@ def _backward_checks(bmod):
             want[0, h // 2] += bmod.attention_backward(q[0, h], k[0, h // 2], v[0, h // 2], do[0, h], 0.5, True)[1]
         return np.allclose(dk, want, rtol=1e-13, atol=1e-14)
 
-    for name, fn in (("autograd", autograd), ("grouped", grouped)):
+    def varlen():
+        rng = np.random.default_rng(11)
+        lengths = [3, 0, 4]
+        cu = np.concatenate([[0], np.cumsum(lengths)])
+        q, do = (rng.standard_normal((7, 4, 3)) for _ in range(2))
+        k, v = (rng.standard_normal((7, 2, 3)) for _ in range(2))
+        dq, dk, dv = bmod.attention_backward_varlen(q, k, v, do, cu, 0.7, True)
+        seq = np.repeat(np.arange(3), lengths)
+        pos = np.arange(7) - cu[seq]
+        allowed = (seq[:, None] == seq[None, :]) & (pos[None, :] <= pos[:, None])
+        qt, kt, vt = (torch.from_numpy(x.transpose(1, 0, 2).copy()).requires_grad_(True) for x in (q, k, v))
+        o = F.scaled_dot_product_attention(qt[None], kt.repeat_interleave(2, 0)[None], vt.repeat_interleave(2, 0)[None],
+                                           attn_mask=torch.from_numpy(allowed), scale=0.7)[0]
+        o.backward(torch.from_numpy(do.transpose(1, 0, 2).copy()))
+        return all(np.allclose(a, t.grad.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-11)
+                   for a, t in ((dq, qt), (dk, kt), (dv, vt)))
+
+    for name, fn in (("autograd", autograd), ("grouped", grouped), ("varlen", varlen)):
         try:
             ok = bool(fn())
         except Exception:
@@ -294,6 +311,11 @@ BACKWARD_MUTANTS = [
     ("dV without transpose", "dv = p.T @ do", "dv = p @ do"),
     ("causal mask dropped in backward", "    if causal:\n        s = np.where(", "    if False:\n        s = np.where("),
     ("grouped gradients overwritten, not summed", "dk[b, g] += bk", "dk[b, g] = bk"),
+    ("varlen KV gradients overwritten, not summed", "dk[a:b, g] += y", "dk[a:b, g] = y"),
+    ("varlen KV head taken as h % Hkv", "            g = h // group\n            x, y, z = attention_backward(q[a:b, h]",
+     "            g = h % hkv\n            x, y, z = attention_backward(q[a:b, h]"),
+    ("varlen keys from the whole pack", "attention_backward(q[a:b, h], k[a:b, g], v[a:b, g], do[a:b, h]",
+     "attention_backward(q[a:b, h], k[:, g][:b - a], v[:, g][:b - a], do[a:b, h]"),
 ]
 
 

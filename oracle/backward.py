@@ -23,14 +23,17 @@ import numpy as np
 from oracle.dense import NEG_INF
 
 
-def attention_backward(q, k, v, do, scale, causal=False):
+def attention_backward(q, k, v, do, scale, causal=False, allowed=None):
     """One head, equal lengths (causal: key j eligible for query i iff
-    j <= i). q, k, v, do: [N, D] float64. Returns dq, dk, dv."""
+    j <= i). q, k, v, do: [N, D] float64. ``allowed`` [N, N] (optional)
+    restricts the eligible pairs further. Returns dq, dk, dv."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     n = q.shape[0]
     s = scale * (q @ k.T)
     if causal:
         s = np.where(np.arange(k.shape[0])[None, :] <= np.arange(n)[:, None], s, NEG_INF)
+    if allowed is not None:
+        s = np.where(np.asarray(allowed, dtype=bool), s, NEG_INF)
     m = s.max(axis=1, keepdims=True) if s.size else np.zeros((n, 1))
     m = np.where(np.isfinite(m), m, 0.0)
     e = np.exp(s - m)
@@ -89,4 +92,34 @@ def attention_backward_varlen(q, k, v, do, cu_seqlens, scale, causal=True):
             dq[a:b, h] = x
             dk[a:b, g] += y
             dv[a:b, g] += z
+    return dq, dk, dv
+
+
+def attention_backward_sparse_bhnd(q, k, v, do, scale, causal=False, left=-1, right=-1, n_global=0,
+                                   block_mask=None, block_q=64, block_k=64):
+    """Gradients of the sparse operator (window, global tokens, block mask;
+    "Attention algorithms and data movement", lessons 06 and 07) on equal
+    lengths: q, do [B, Hq, N, D]; k, v [B, Hkv, N, D]; block_mask None,
+    [nqb, nkb] shared by every query head, or [Hq, nqb, nkb]. Eligibility is
+    ``dense.sparse_eligibility`` with Nq = Nk; rows with no eligible key
+    contribute nothing. KV-head gradients sum their query heads in order."""
+    from oracle.dense import sparse_eligibility
+    b_, hq, n = q.shape[0], q.shape[1], q.shape[2]
+    hkv = k.shape[1]
+    group = hq // hkv
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for h in range(hq):
+        bm = None
+        if block_mask is not None:
+            bm = np.asarray(block_mask)
+            bm = bm[h] if bm.ndim == 3 else bm
+        allowed = sparse_eligibility(n, n, causal, left, right, n_global, bm, block_q, block_k)
+        g = h // group
+        for b in range(b_):
+            x, y, z = attention_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, False, allowed)
+            dq[b, h] = x
+            dk[b, g] += y
+            dv[b, g] += z
     return dq, dk, dv

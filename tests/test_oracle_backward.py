@@ -121,3 +121,58 @@ def test_varlen_vs_autograd_through_packed_mask(causal):
     np.testing.assert_allclose(dq, qt.grad.numpy().transpose(1, 0, 2), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(dk, kt.grad.numpy().transpose(1, 0, 2), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(dv, vt.grad.numpy().transpose(1, 0, 2), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sparse_vs_autograd_through_the_mask(causal):
+    """Window, global tokens and a per-head block mask with grouped heads:
+    torch float64 autograd through SDPA with the same boolean mask, on KV
+    heads repeated over their query heads. The block mask keeps every
+    diagonal block, so every row has an eligible key."""
+    rng = np.random.default_rng(41)
+    n, hq, hkv, d = 40, 4, 2, 5
+    q, do = rng.standard_normal((1, hq, n, d)), rng.standard_normal((1, hq, n, d))
+    k, v = rng.standard_normal((1, hkv, n, d)), rng.standard_normal((1, hkv, n, d))
+    bm = rng.integers(0, 2, size=(hq, 5, 5)).astype(np.uint8)
+    for h in range(hq):
+        np.fill_diagonal(bm[h], 1)
+    dq, dk, dv = backward.attention_backward_sparse_bhnd(q, k, v, do, 0.4, causal, 6, 3, 2, bm, 8, 8)
+    mask = torch.from_numpy(np.stack([dense.sparse_eligibility(n, n, causal, 6, 3, 2, bm[h], 8, 8)
+                                      for h in range(hq)]))
+    assert mask.any(dim=2).all()
+    qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    o = F.scaled_dot_product_attention(qt, kt.repeat_interleave(2, 1), vt.repeat_interleave(2, 1),
+                                       attn_mask=mask[None], scale=0.4)
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_sparse_rows_without_keys_contribute_nothing():
+    """A query block whose mask row is all zero has no eligible key: its dQ
+    is exactly 0 and dK, dV equal those of the same problem with its dO set
+    to zero (no other row is affected)."""
+    rng = np.random.default_rng(42)
+    n, d = 32, 4
+    q, k, v, do = (rng.standard_normal((1, 1, n, d)) for _ in range(4))
+    bm = np.ones((4, 4), dtype=np.uint8)
+    bm[1, :] = 0                                          # rows 8..15: no key
+    dq, dk, dv = backward.attention_backward_sparse_bhnd(q, k, v, do, 0.5, True, -1, -1, 0, bm, 8, 8)
+    assert np.all(dq[0, 0, 8:16] == 0.0)
+    do2 = do.copy()
+    do2[0, 0, 8:16] = 0.0
+    _, dk2, dv2 = backward.attention_backward_sparse_bhnd(q, k, v, do2, 0.5, True, -1, -1, 0, bm, 8, 8)
+    np.testing.assert_array_equal(dk, dk2)
+    np.testing.assert_array_equal(dv, dv2)
+
+
+def test_unrestricted_sparse_is_dense_backward():
+    rng = np.random.default_rng(43)
+    q, do = rng.standard_normal((2, 4, 20, 3)), rng.standard_normal((2, 4, 20, 3))
+    k, v = rng.standard_normal((2, 2, 20, 3)), rng.standard_normal((2, 2, 20, 3))
+    for causal in (False, True):
+        a = backward.attention_backward_sparse_bhnd(q, k, v, do, 0.5, causal)
+        b = backward.attention_backward_bhnd(q, k, v, do, 0.5, causal)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)

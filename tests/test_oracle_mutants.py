@@ -296,7 +296,22 @@ def _backward_checks(bmod):
         return all(np.allclose(a, t.grad.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-11)
                    for a, t in ((dq, qt), (dk, kt), (dv, vt)))
 
-    for name, fn in (("autograd", autograd), ("grouped", grouped), ("varlen", varlen)):
+    def sparse():
+        from oracle import dense as dn
+        rng = np.random.default_rng(12)
+        n = 24
+        q, do = (rng.standard_normal((1, 2, n, 3)) for _ in range(2))
+        k, v = (rng.standard_normal((1, 1, n, 3)) for _ in range(2))
+        bm = np.array([[[1, 0, 1], [1, 1, 0], [0, 1, 1]], [[1, 1, 0], [0, 1, 0], [1, 0, 1]]], dtype=np.uint8)
+        dq, dk, dv = bmod.attention_backward_sparse_bhnd(q, k, v, do, 0.6, True, 5, -1, 1, bm, 8, 8)
+        mask = torch.from_numpy(np.stack([dn.sparse_eligibility(n, n, True, 5, -1, 1, bm[h], 8, 8) for h in range(2)]))
+        qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+        o = F.scaled_dot_product_attention(qt, kt.repeat_interleave(2, 1), vt.repeat_interleave(2, 1),
+                                           attn_mask=mask[None], scale=0.6)
+        o.backward(torch.from_numpy(do))
+        return all(np.allclose(a, t.grad.numpy(), rtol=1e-10, atol=1e-11) for a, t in ((dq, qt), (dk, kt), (dv, vt)))
+
+    for name, fn in (("autograd", autograd), ("grouped", grouped), ("varlen", varlen), ("sparse", sparse)):
         try:
             ok = bool(fn())
         except Exception:
@@ -314,6 +329,10 @@ BACKWARD_MUTANTS = [
     ("varlen KV gradients overwritten, not summed", "dk[a:b, g] += y", "dk[a:b, g] = y"),
     ("varlen KV head taken as h % Hkv", "            g = h // group\n            x, y, z = attention_backward(q[a:b, h]",
      "            g = h % hkv\n            x, y, z = attention_backward(q[a:b, h]"),
+    ("sparse eligibility ignored in backward", "        s = np.where(np.asarray(allowed, dtype=bool), s, NEG_INF)",
+     "        s = s"),
+    ("sparse block mask of head 0 for every head", "            bm = bm[h] if bm.ndim == 3 else bm",
+     "            bm = bm[0] if bm.ndim == 3 else bm"),
     ("varlen keys from the whole pack", "attention_backward(q[a:b, h], k[a:b, g], v[a:b, g], do[a:b, h]",
      "attention_backward(q[a:b, h], k[:, g][:b - a], v[:, g][:b - a], do[a:b, h]"),
 ]

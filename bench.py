@@ -474,6 +474,33 @@ def varlen_backward_extra(steps):
             "flop_convention": "2.5x the forward's causal 2*L^2*D per query head"}
 
 
+def sparse_backward_extra(steps):
+    """Backward of the causal sliding window (2048 keys) united with 64
+    global tokens, B=1, H=16, N=16384, D=128 bf16, on the forward's own O and
+    lse. FLOPs: 2.5x the forward's kept-pair count at 4*D each."""
+    from exact_tiled_attention_sattn_amd import sattn_fwd_sparse, sattn_bwd_sparse
+    h, d, n, w, ng = 16, 128, 16384, 2048, 64
+    scale = W.scale_f32(d)
+    q, k, v = (x.to(DEV) for x in W.qkv((1, h, n, d), (1, h, n, d), "bf16", 10))
+    do = W.randn((1, h, n, d), "bf16", torch.Generator().manual_seed(12)).to(DEV)
+    o, lse = sattn_fwd_sparse(q, k, v, causal=True, window=(w - 1, -1), n_global=ng, scale=scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((1, h, n), dtype=torch.float32, device=DEV)
+    fn = lambda: sattn_bwd_sparse(q, k, v, o, do, lse, causal=True, window=(w - 1, -1), n_global=ng,  # noqa: E731
+                                  scale=scale, dq=dq, dk=dk, dv=dv, delta=delta)
+    fn()
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
+    ms = float(np.mean(time_launches(fn, steps, 2)))
+    pairs = sum((i + 1) if i < ng else min(i + 1, w) + ng - max(0, ng - max(0, i - w + 1)) for i in range(n)) * h
+    del q, k, v, do, dq, dk, dv, o
+    torch.cuda.empty_cache()
+    fl = 2.5 * 4 * d * pairs
+    return {"workload": "backward of causal_window2048_global64_16x16384x128_bf16", "ms_mean": ms,
+            "TFLOPs": fl / ms / 1e9, "frac_of_bf16_peak": fl / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "flop_convention": "2.5x the forward's kept pairs at 4*D"}
+
+
 def cpu_baseline(budget_s):
     """The FP64 oracle on sampled query rows of the batched workload, both
     variants, on the host cores, scaled to TFLOP/s by the sampled fraction."""
@@ -644,6 +671,8 @@ def main():
         extras["backward"] = backward_extra(max(3, min(args.steps, 10)))
         log("backward: packed varlen GQA")
         extras["varlen_backward"] = varlen_backward_extra(max(3, min(args.steps, 10)))
+        log("backward: sliding window + global tokens")
+        extras["sparse_backward"] = sparse_backward_extra(max(3, min(args.steps, 10)))
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen", "sattn_fwd_cache",
-    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse", "sattn_bwd", "sattn_bwd_varlen",
+    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse", "sattn_bwd", "sattn_bwd_varlen", "sattn_bwd_sparse",
     "SattnError", "library", "LIB_PATH", "STATUS",
 ]
 
@@ -76,6 +76,9 @@ def library():
     lib.sattn_bwd_varlen.restype = i32
     lib.sattn_bwd_varlen.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                      i64, i32, ctypes.c_float, vp]
+    lib.sattn_bwd_sparse.restype = i32
+    lib.sattn_bwd_sparse.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
+                                     i64, i64, i64, vp, i64, i64, i64, ctypes.c_float, vp]
     lib.sattn_fwd_sparse.restype = i32
     lib.sattn_fwd_sparse.argtypes = [i32, vp, vp, vp, vp, fp, i64, i64, i64, i64, i64, i64, i32, i64, i64, i64,
                                      vp, i64, i64, i64, ctypes.c_float, vp]
@@ -464,4 +467,51 @@ def sattn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen=None, causal=
                                     _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_dev),
                                     cu_dev.numel() - 1, t_, max_seqlen, hq, hkv, d, int(bool(causal)),
                                     _scale(scale, d), _stream(dev)))
+    return dq, dk, dv
+
+
+def sattn_bwd_sparse(q, k, v, o, dout, lse, causal=False, window=(-1, -1), n_global=0, block_mask=None,
+                     block_q=64, block_k=64, scale=None, dq=None, dk=None, dv=None, delta=None):
+    """Gradients of sum(dout * o) for o, lse = sattn_fwd_sparse(q, k, v, ...)
+    with Nq = Nk (the same window, n_global, block mask and blocks).
+    q, o, dout [B,Hq,N,D]; k, v [B,Hkv,N,D]; lse [B,Hq,N] float32;
+    ``delta`` is a float32 [B,Hq,N] workspace.
+
+    Returns (dq, dk, dv) in q's dtype."""
+    lib = library()
+    _dev_tensor(q, "q", ndim=4)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q must be float16 or bfloat16")
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _dev_tensor(t, name, q.dtype, 4)
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (b, hkv, n, d) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q/o/dout must be [B,Hq,N,D] and k/v [B,Hkv,N,D]")
+    _dev_tensor(lse, "lse", torch.float32, 3)
+    if lse.shape != (b, hq, n):
+        raise ValueError("lse must be [B, Hq, N]")
+    dev = _same_device(q, k, v, o, dout, lse, dq, dk, dv, delta, block_mask)
+    heads = 0
+    if block_mask is not None:
+        _dev_tensor(block_mask, "block_mask", torch.uint8)
+        if block_mask.dim() == 2:
+            block_mask = block_mask.unsqueeze(0)
+        nqb, nkb = -(-n // int(block_q)), -(-n // int(block_k))
+        if block_mask.dim() != 3 or tuple(block_mask.shape[1:]) != (nqb, nkb):
+            raise ValueError("block_mask must be [nqb, nkb] or [heads, %d, %d]" % (nqb, nkb))
+        heads = block_mask.shape[0]
+    dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q.dtype, 4)
+    dk = torch.empty_like(k) if dk is None else _dev_tensor(dk, "dk", q.dtype, 4)
+    dv = torch.empty_like(v) if dv is None else _dev_tensor(dv, "dv", q.dtype, 4)
+    delta = torch.empty((b, hq, n), dtype=torch.float32, device=dev) if delta is None else \
+        _dev_tensor(delta, "delta", torch.float32, 3)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape or delta.shape != (b, hq, n):
+        raise ValueError("gradient/workspace shape mismatch")
+    left, right = window
+    with torch.cuda.device(dev):
+        _check(lib.sattn_bwd_sparse(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                    _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, n, d,
+                                    int(bool(causal)), int(left), int(right), int(n_global), _ptr(block_mask),
+                                    heads, int(block_q), int(block_k), _scale(scale, d), _stream(dev)))
     return dq, dk, dv

@@ -43,9 +43,43 @@ struct BwdParams {
   // [cu_seqlens[s], cu_seqlens[s+1]) and positions count from its start
   const int32_t* cu_seqlens;
   int nseq, total;
+  // sparse (dense layout, Nq = Nk): key j is eligible for query i iff
+  // (i - win_left <= j <= i + win_right, a negative bound unlimited) or
+  // j < n_global or i < n_global, and block (i / bm_q, j / bm_k) of query
+  // head h is active in bmask (if given; h reads bmask + h * bm_hstride,
+  // bm_nkb blocks per row), and j <= i when causal
+  int win_left, win_right, n_global;
+  const uint8_t* bmask;
+  int bm_q, bm_k, bm_nkb;
+  int64_t bm_hstride;
   float c;              // scale * log2(e)
   float scale;
 };
+
+// Row layouts of the backward kernels: [B, H, N, D] slices, packed
+// variable-length [T, H, D] sequences, and [B, H, N, D] slices under the
+// sparse operator's eligibility.
+enum { BWD_DENSE = 0, BWD_VARLEN = 1, BWD_SPARSE = 2 };
+
+// The sparse rule on a block of rows [i0, i1] and keys [j0, j1] (window and
+// global tokens only; causality and the block mask are checked apart):
+// some pair eligible, every pair eligible, and one pair.
+__device__ __forceinline__ bool sparse_any(const BwdParams& p, int i0, int i1, int j0, int j1) {
+  const bool win = (p.win_left < 0 || j1 >= i0 - p.win_left) && (p.win_right < 0 || j0 <= i1 + p.win_right);
+  return win || j0 < p.n_global || i0 < p.n_global;
+}
+__device__ __forceinline__ bool sparse_all(const BwdParams& p, int i0, int i1, int j0, int j1) {
+  const bool win = (p.win_left < 0 || j0 >= i1 - p.win_left) && (p.win_right < 0 || j1 <= i0 + p.win_right);
+  return win || j1 < p.n_global || i1 < p.n_global;
+}
+__device__ __forceinline__ bool sparse_pair(const BwdParams& p, int i, int j) {
+  const bool win = (p.win_left < 0 || j >= i - p.win_left) && (p.win_right < 0 || j <= i + p.win_right);
+  return win || j < p.n_global || i < p.n_global;
+}
+// Block-mask bit of query i and key j for query head h (true without a mask).
+__device__ __forceinline__ bool sparse_bit(const BwdParams& p, int h, int i, int j) {
+  return !p.bmask || p.bmask[(int64_t)h * p.bm_hstride + (int64_t)(i / p.bm_q) * p.bm_nkb + j / p.bm_k] != 0;
+}
 
 // One 64-row tile of a [row][D] tensor into LDS (swizzled like the forward's
 // K/V tiles): each wave moves its NI 1 KiB pieces.
@@ -72,7 +106,7 @@ struct TileLoader {
 };
 
 // ---------------------------------------------------------------- dQ
-template <class E, int D, bool CAUSAL, bool VARLEN>
+template <class E, int D, bool CAUSAL, int LAYOUT>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   constexpr int NW = 4, BM = 128, BN = 64;
   constexpr int KK = D / 16, KB = BN / 32, DB = D / 32;
@@ -85,9 +119,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   // sequence, then query tile, then the query heads of the group, as in the
   // varlen forward. Offsets in elements: qbase is row q_pos0 of q/o/dout/dq,
   // kvbase key 0 of k/v, lbase row q_pos0 of lse/Delta.
-  int len, q_pos0;
+  int len, q_pos0, qh;
   int64_t qbase, kvbase, lbase, q_rs, kv_rs;
-  if constexpr (VARLEN) {
+  if constexpr (LAYOUT == BWD_VARLEN) {
     const int grp = p.hq / p.hkv;
     const int lin = xcd_linear(blockIdx.x);
     const int per_g = p.nseq * p.nqt * grp;
@@ -97,6 +131,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     const int r2 = r1 % (p.nqt * grp);
     const int qt = p.nqt - 1 - r2 / grp;
     const int h = g * grp + r2 % grp;
+    qh = h;
     // clamp the table so that a malformed one cannot address outside [0, T)
     int a = p.cu_seqlens[sq], e = p.cu_seqlens[sq + 1];
     a = min(max(a, 0), p.total);
@@ -115,6 +150,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     const int qt = p.nqt - 1 - lin % p.nqt;
     const int b = slice / p.hq, h = slice % p.hq;
     const int kvs = b * p.hkv + h / (p.hq / p.hkv);
+    qh = h;
     len = p.n;
     q_pos0 = qt * BM;
     q_rs = D;
@@ -189,12 +225,36 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
       tofs[x][db] = key * D + (((d0 >> 3) ^ swz<D>(key)) * 8) + (d0 & 7);
     }
 
-  auto step = [&](int t, const uint16_t* cur, uint16_t* nxt) {
+  // Key tiles walked: [0, ntiles), or under the sparse operator (no global
+  // query among the rows) the global-key prefix [0, npre) and then the
+  // window band [band0, band0 + nsteps - npre).
+  int npre = 0, band0 = 0, nsteps = ntiles;
+  if constexpr (LAYOUT == BWD_SPARSE) {
+    if (q_pos0 >= p.n_global) {
+      npre = min(ntiles, (p.n_global + BN - 1) / BN);
+      const int lo = p.win_left < 0 ? 0 : max(0, q_pos0 - p.win_left) / BN;
+      const int hi = p.win_right < 0 ? ntiles : min(ntiles, (q_pos0 + BM - 1 + p.win_right) / BN + 1);
+      band0 = max(npre, lo);
+      nsteps = npre + max(0, hi - band0);
+    }
+  }
+  auto tile_of = [&](int idx) { return idx < npre ? idx : band0 + (idx - npre); };
+
+  auto step = [&](int idx, const uint16_t* cur, uint16_t* nxt) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < ntiles) issue_tile(t + 1, nxt);
-    const int kt0 = t * BN;
+    if (idx + 1 < nsteps) issue_tile(tile_of(idx + 1), nxt);
+    const int kt0 = tile_of(idx) * BN;
     if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
+    bool edge = kt0 + BN > len || (CAUSAL && kt0 + BN - 1 > q_pos0 + wave * 32);
+    if constexpr (LAYOUT == BWD_SPARSE) {
+      // the wave's 32 rows lie in one mask row block and the tile's keys in
+      // one key block (block_q % 32 == 0, block_k % 64 == 0)
+      const int i0 = q_pos0 + wave_u * 32, i1 = min(i0 + 31, len - 1);
+      const int j1 = min(kt0 + BN, len) - 1;
+      if (!sparse_bit(p, qh, i0, kt0) || !sparse_any(p, i0, i1, kt0, j1)) return;
+      edge = edge || !sparse_all(p, i0, i1, kt0, j1);
+    }
     const uint16_t* sK = cur;
     const uint16_t* sV = cur + TILE;
     // S^T = K Q^T and dP^T = V dO^T (keys x queries, one query per lane)
@@ -213,7 +273,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
       }
     }
     // P = exp2(S c - lse log2 e) on eligible keys; dS = P (dP - Delta)
-    const bool edge = kt0 + BN > len || (CAUSAL && kt0 + BN - 1 > q_pos0 + wave * 32);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -221,7 +280,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
         float pr = fast_exp2(fmaf(s[kb][r], p.c, -lse2));
         if (edge) {
           const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= len || (CAUSAL && key > my_pos)) pr = 0.f;
+          if (key >= len || (CAUSAL && key > my_pos) || (LAYOUT == BWD_SPARSE && !sparse_pair(p, my_pos, key)))
+            pr = 0.f;
         }
         s[kb][r] = pr * (dp[kb][r] - delta);
       }
@@ -242,14 +302,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
         }
       }
   };
-  if (ntiles > 0) {
-    issue_tile(0, sbuf0);
+  if (nsteps > 0) {
+    issue_tile(tile_of(0), sbuf0);
     int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
+    for (; t + 1 < nsteps; t += 2) {
       step(t, sbuf0, sbuf1);
       step(t + 1, sbuf1, sbuf0);
     }
-    if (t < ntiles) step(t, sbuf0, sbuf1);
+    if (t < nsteps) step(t, sbuf0, sbuf1);
   }
   if (!row_ok) return;
   uint16_t* op = p.dq + qbase + (int64_t)qrow * q_rs;
@@ -264,8 +324,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <class E, int D, bool CAUSAL, bool VARLEN>
+template <class E, int D, bool CAUSAL, int LAYOUT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr bool VARLEN = LAYOUT == BWD_VARLEN;
+  constexpr bool SPARSE = LAYOUT == BWD_SPARSE;
   // queries per step, in 64-row sub-tiles (128 measured no faster)
   constexpr int NW = 4, BNK = 128, BMQ = 64;
   constexpr int KK = D / 16, DB = D / 32;
@@ -346,17 +408,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       adv[db][r] = 0.f;
     }
 
-  // query tiles: every query head of the group, causal from the tile holding k0
+  // query tiles: every query head of the group, causal from the tile holding
+  // k0; under the sparse operator (no global key among the keys) only the
+  // tiles of global queries [t_begin, t_begin + npre) and then the window
+  // band from band0
   const int t_begin = CAUSAL ? k0 / BMQ : 0;
   const int nqt = (len + BMQ - 1) / BMQ;
-  const int per_head = nqt - t_begin;
+  int per_head = nqt - t_begin, npre = 0, band0 = t_begin;
+  if constexpr (SPARSE) {
+    if (k0 >= p.n_global) {
+      const int pre_hi = max(t_begin, min(nqt, (p.n_global + BMQ - 1) / BMQ));
+      npre = pre_hi - t_begin;
+      const int lo = p.win_right < 0 ? 0 : max(0, k0 - p.win_right) / BMQ;
+      const int hi = p.win_left < 0 ? nqt : min(nqt, (k0 + BNK - 1 + p.win_left) / BMQ + 1);
+      band0 = max(pre_hi, lo);
+      per_head = npre + max(0, hi - band0);
+    }
+  }
+  auto qtile_of = [&](int i) { return i < npre ? t_begin + i : band0 + (i - npre); };
   const int nsteps = per_head * grp;
   const uint32_t row_bytes = (uint32_t)q_rs * 2u;
   TileLoader<D, NW> ld;
   ld.init(wave, lane, row_bytes);
   auto issue_step = [&](int it, uint16_t* sb) {
     const int hh = g * grp + it / per_head;
-    const int t = t_begin + it % per_head;
+    const int t = qtile_of(it % per_head);
     const int q0 = t * BMQ;
     const int rows = min(BMQ, len - q0);
     const int64_t qoff = qhead(hh) + (int64_t)q0 * q_rs;
@@ -438,7 +514,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       float x = fast_exp2(fmaf(s[r], p.c, -lse4[r >> 2][r & 3] * kLog2e));
       if (edge) {
         const int qi = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (qi >= len || (CAUSAL && my_key > qi)) x = 0.f;
+        if (qi >= len || (CAUSAL && my_key > qi) || (SPARSE && !sparse_pair(p, qi, my_key))) x = 0.f;
       }
       pr[r] = x;
       ds[r] = x * (dp[r] - del4[r >> 2][r & 3]);
@@ -472,8 +548,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (it + 1 < nsteps) issue_step(it + 1, nxt);
-    const int q0 = (t_begin + it % per_head) * BMQ;
+    const int q0 = qtile_of(it % per_head) * BMQ;
+    const int hh = g * grp + it / per_head;
     if (!wave_active) return;
+    // sparse: need / no mask needed for 32-query block qb0 against the wave's
+    // keys (one mask row block, one key block)
+    const int wkey1 = min(wave_first_key + 31, len - 1);
+    auto blk_need = [&](int qb0) {
+      return qb0 < len && sparse_bit(p, hh, qb0, wave_first_key) &&
+             sparse_any(p, qb0, min(qb0 + 31, len - 1), wave_first_key, wkey1);
+    };
+    auto blk_full = [&](int qb0) {
+      return blk_need(qb0) && sparse_all(p, qb0, min(qb0 + 31, len - 1), wave_first_key, wkey1);
+    };
     const uint16_t* sQ = cur;
     const uint16_t* sD = cur + TILE;
     const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
@@ -482,7 +569,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // the wave need no mask: one branch-free body in which the second
     // block's S/dP products overlap the first block's exps, and the first
     // block's dV/dK products the second block's.
-    if (q0 + BMQ <= len && (!CAUSAL || q0 >= wave_first_key + 31)) {
+    if (q0 + BMQ <= len && (!CAUSAL || q0 >= wave_first_key + 31) && (!SPARSE || (blk_full(q0) && blk_full(q0 + 32)))) {
       static_assert(BMQ == 64, "the unmasked body takes two 32-query blocks");
       f32x16 s0, dp0, s1, dp1;
       u32x4 pb0[2], sb0[2], pb1[2], sb1[2];
@@ -518,10 +605,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     for (int qb = 0; qb < BMQ / 32; ++qb) {
       const int qb0 = q0 + qb * 32;
       if (CAUSAL && qb0 + 31 < wave_first_key) continue;   // every query of the block precedes the wave's keys
+      if (SPARSE && !blk_need(qb0)) continue;
       f32x16 s, dp;
       u32x4 pb[2], sb[2];
       sd_mfma(sQ, sD, qb, s, dp);
-      probs(sL, sE, qb, s, dp, pb, sb, qb0 + 32 > len || (CAUSAL && qb0 < wave_first_key + 31), qb0);
+      probs(sL, sE, qb, s, dp, pb, sb,
+            qb0 + 32 > len || (CAUSAL && qb0 < wave_first_key + 31) || (SPARSE && !blk_full(qb0)), qb0);
       dvdk_mfma(sQ, sD, qb, pb, sb);
     }
   };
@@ -555,7 +644,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 #define SATTN_BWD_INST2(E_, D_, C_, V_)                                      \
   template __global__ void bwd_dq_kernel<E_, D_, C_, V_>(const BwdParams); \
   template __global__ void bwd_dkdv_kernel<E_, D_, C_, V_>(const BwdParams);
-#define SATTN_BWD_INST(E_, D_, C_) SATTN_BWD_INST2(E_, D_, C_, false) SATTN_BWD_INST2(E_, D_, C_, true)
+#define SATTN_BWD_INST(E_, D_, C_) \
+  SATTN_BWD_INST2(E_, D_, C_, BWD_DENSE) SATTN_BWD_INST2(E_, D_, C_, BWD_VARLEN) SATTN_BWD_INST2(E_, D_, C_, BWD_SPARSE)
 SATTN_BWD_INST(Bf16, 32, false) SATTN_BWD_INST(Bf16, 32, true) SATTN_BWD_INST(Bf16, 64, false)
 SATTN_BWD_INST(Bf16, 64, true) SATTN_BWD_INST(Bf16, 128, false) SATTN_BWD_INST(Bf16, 128, true)
 SATTN_BWD_INST(F16, 32, false) SATTN_BWD_INST(F16, 32, true) SATTN_BWD_INST(F16, 64, false)

@@ -150,28 +150,28 @@ void dispatch_split(int dtype, int64_t D, const FwdParams& p, int64_t grid, hipS
 }
 
 // dQ first: it also writes Delta, which the dK/dV kernel reads (stream order).
-template <class E, int D, bool VARLEN>
+template <class E, int D, int LAYOUT>
 void launch_bwd(const BwdParams& p, bool causal, int64_t grid_q, int64_t grid_kv, hipStream_t s) {
   if (causal) {
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, VARLEN>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, VARLEN>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, LAYOUT>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, VARLEN>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, VARLEN>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, LAYOUT>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
   }
 }
 
-template <bool VARLEN>
+template <int LAYOUT>
 void dispatch_bwd(int dtype, int64_t D, bool causal, const BwdParams& p, int64_t grid_q, int64_t grid_kv,
                   hipStream_t s) {
   if (dtype == SATTN_BF16) {
-    if (D == 32) launch_bwd<Bf16, 32, VARLEN>(p, causal, grid_q, grid_kv, s);
-    else if (D == 64) launch_bwd<Bf16, 64, VARLEN>(p, causal, grid_q, grid_kv, s);
-    else launch_bwd<Bf16, 128, VARLEN>(p, causal, grid_q, grid_kv, s);
+    if (D == 32) launch_bwd<Bf16, 32, LAYOUT>(p, causal, grid_q, grid_kv, s);
+    else if (D == 64) launch_bwd<Bf16, 64, LAYOUT>(p, causal, grid_q, grid_kv, s);
+    else launch_bwd<Bf16, 128, LAYOUT>(p, causal, grid_q, grid_kv, s);
   } else {
-    if (D == 32) launch_bwd<F16, 32, VARLEN>(p, causal, grid_q, grid_kv, s);
-    else if (D == 64) launch_bwd<F16, 64, VARLEN>(p, causal, grid_q, grid_kv, s);
-    else launch_bwd<F16, 128, VARLEN>(p, causal, grid_q, grid_kv, s);
+    if (D == 32) launch_bwd<F16, 32, LAYOUT>(p, causal, grid_q, grid_kv, s);
+    else if (D == 64) launch_bwd<F16, 64, LAYOUT>(p, causal, grid_q, grid_kv, s);
+    else launch_bwd<F16, 128, LAYOUT>(p, causal, grid_q, grid_kv, s);
   }
 }
 
@@ -484,9 +484,10 @@ int sattn_fwd_sparse(int dtype, const void* q, const void* k, const void* v, voi
   return cache_impl(dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, qs, ks, causal, scale, stream, &sp);
 }
 
-int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
-              const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
-              int64_t N, int64_t D, int causal, float scale, void* stream) {
+static int bwd_impl(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq,
+                    int64_t Hkv, int64_t N, int64_t D, int causal, float scale, void* stream,
+                    const SparseSpec* sp = nullptr) {
   int st = check_common(dtype, D, scale);
   if (st) return st;
   if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return fail(SATTN_ERR_SHAPE, "negative size");
@@ -502,11 +503,27 @@ int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
     return fail(SATTN_ERR_ALIGN, "16-bit tensors need 16-byte, lse/delta 4-byte alignment");
-  Range ins[6] = {range_of(q, qbytes, "q"), range_of(k, kvbytes, "k"), range_of(v, kvbytes, "v"),
-                  range_of(o, qbytes, "o"), range_of(dout, qbytes, "dout"), range_of(lse, qrows * 4, "lse")};
+  int64_t nkb = 0, mbytes = 0;
+  if (sp) {
+    if (sp->left < -1 || sp->right < -1 || sp->n_global < 0 || sp->left >= kMaxLen || sp->right >= kMaxLen ||
+        sp->n_global >= kMaxLen)
+      return fail(SATTN_ERR_VALUE, "window bounds must be >= -1 and n_global >= 0");
+    if (sp->mask) {
+      if (sp->block_q <= 0 || sp->block_q % 32 != 0 || sp->block_k <= 0 || sp->block_k % 64 != 0 ||
+          sp->block_q >= kMaxLen || sp->block_k >= kMaxLen)
+        return fail(SATTN_ERR_UNSUPPORTED, "block_q must be a positive multiple of 32 and block_k of 64");
+      if (sp->mask_heads != 1 && sp->mask_heads != Hq) return fail(SATTN_ERR_SHAPE, "mask_heads must be 1 or Hq");
+      const int64_t nqb = (N + sp->block_q - 1) / sp->block_q;
+      nkb = (N + sp->block_k - 1) / sp->block_k;
+      if (!product({sp->mask_heads, nqb, nkb}, &mbytes)) return fail(SATTN_ERR_SHAPE, "size overflow");
+    }
+  }
+  Range ins[7] = {range_of(q, qbytes, "q"),       range_of(k, kvbytes, "k"),          range_of(v, kvbytes, "v"),
+                  range_of(o, qbytes, "o"),       range_of(dout, qbytes, "dout"),     range_of(lse, qrows * 4, "lse"),
+                  range_of(sp ? sp->mask : nullptr, mbytes, "block_mask")};
   Range outs[4] = {range_of(dq, qbytes, "dq"), range_of(dk, kvbytes, "dk"), range_of(dv, kvbytes, "dv"),
                    range_of(delta, qrows * 4, "delta")};
-  if ((st = check_alias(ins, 6, outs, 4))) return st;
+  if ((st = check_alias(ins, 7, outs, 4))) return st;
   BwdParams p{};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -527,8 +544,35 @@ int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void
   p.scale = scale;
   const int64_t grid_q = B * Hq * p.nqt, grid_kv = B * Hkv * p.nkt;
   if (grid_q >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
-  dispatch_bwd<false>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
+  if (sp) {
+    p.win_left = (int)sp->left;
+    p.win_right = (int)sp->right;
+    p.n_global = (int)sp->n_global;
+    p.bmask = sp->mask;
+    p.bm_q = (int)sp->block_q;
+    p.bm_k = (int)sp->block_k;
+    p.bm_nkb = (int)nkb;
+    p.bm_hstride = (sp->mask && sp->mask_heads > 1) ? mbytes / sp->mask_heads : 0;
+    dispatch_bwd<BWD_SPARSE>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
+  } else {
+    dispatch_bwd<BWD_DENSE>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
+  }
   return launch_status();
+}
+
+int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+              int64_t N, int64_t D, int causal, float scale, void* stream) {
+  return bwd_impl(dtype, q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale, stream);
+}
+
+int sattn_bwd_sparse(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t N, int64_t D, int causal, int64_t win_left, int64_t win_right,
+                     int64_t n_global, const uint8_t* block_mask, int64_t mask_heads, int64_t block_q,
+                     int64_t block_k, float scale, void* stream) {
+  const SparseSpec sp{win_left, win_right, n_global, block_mask, mask_heads, block_q, block_k};
+  return bwd_impl(dtype, q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale, stream, &sp);
 }
 
 int sattn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -583,7 +627,7 @@ int sattn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, con
   p.total = (int)T;
   p.c = scale * kLog2e;
   p.scale = scale;
-  dispatch_bwd<true>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
+  dispatch_bwd<BWD_VARLEN>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
   return launch_status();
 }
 

@@ -225,6 +225,32 @@ int sattn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, con
                      float scale, void* stream);
 
 /*
+ * Backward pass of sattn_fwd_sparse on equal lengths (Nq = Nk = N): the same
+ * gradients as sattn_bwd with the sparse operator's eligibility ("Attention
+ * algorithms and data movement", lesson 06: block sparsity with skipped
+ * tiles; lesson 07: sliding windows and global tokens).
+ *
+ *   q, o, dout, dq : [B, Hq, N, D];  k, v, dk, dv : [B, Hkv, N, D]  (dtype).
+ *   lse            : [B, Hq, N] float32, as written by sattn_fwd_sparse with
+ *                    Nq = Nk = N for the same inputs, rule and scale (rows
+ *                    with no eligible key carry -inf and get dq = 0).
+ *   delta          : [B, Hq, N] float32 workspace (caller-owned, overwritten).
+ *   win_left, win_right, n_global, block_mask, mask_heads, block_q, block_k:
+ *                    exactly as in sattn_fwd_sparse (with Nq = Nk = N).
+ * Key tiles outside a query tile's window band and global prefix are not
+ * visited (dQ), nor query tiles outside a key tile's band (dK/dV); blocks
+ * whose mask bit is clear are skipped. Two launches on `stream`, no atomics.
+ * Errors as sattn_bwd plus SATTN_ERR_VALUE (window bounds < -1, n_global < 0),
+ * SATTN_ERR_UNSUPPORTED (block sizes), SATTN_ERR_SHAPE (mask_heads not 1 or
+ * Hq) and SATTN_ERR_ALIAS (an output over the mask).
+ */
+int sattn_bwd_sparse(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq,
+                     int64_t Hkv, int64_t N, int64_t D, int causal, int64_t win_left, int64_t win_right,
+                     int64_t n_global, const uint8_t* block_mask, int64_t mask_heads, int64_t block_q,
+                     int64_t block_k, float scale, void* stream);
+
+/*
  * Sparse attention: sattn_fwd_cache restricted to a sliding window, global
  * tokens and a block mask ("Attention algorithms and data movement", lesson
  * 06: count active blocks, block sparsity is a changed operator tested

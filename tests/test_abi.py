@@ -306,3 +306,30 @@ def test_bwd_zero_sizes_ok_without_pointers(lib):
     assert _bwd(lib, b=0, **nulls) == 0
     assert _bwd_varlen(lib, t=0, s=0, max_seqlen=0, cu=0, **nulls) == 0
     assert _bwd_varlen(lib, s=0, cu=0, **nulls) == 0
+
+
+def _bwd_sparse(lib, left=-1, right=-1, g=0, mask=0x700000 + 4096, heads=1, bq=64, bk=64, hq=2, n=8, **ptrs):
+    a = dict(BWD_PTRS)
+    a.update(ptrs)
+    return lib.sattn_bwd_sparse(1, *(_bp(a[x]) for x in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk",
+                                                          "dv")),
+                                1, hq, 1, n, 64, 1, left, right, g, _bp(mask), heads, bq, bk, F32(0.125), NULL)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(left=-2), "SATTN_ERR_VALUE"),
+    (dict(g=-1), "SATTN_ERR_VALUE"),
+    (dict(bq=48), "SATTN_ERR_UNSUPPORTED"),
+    (dict(bk=96), "SATTN_ERR_UNSUPPORTED"),
+    (dict(heads=3), "SATTN_ERR_SHAPE"),
+    (dict(delta=0x700000 + 4096), "SATTN_ERR_ALIAS"),     # workspace over the mask
+    (dict(dq=0), "SATTN_ERR_NULL"),
+    (dict(heads=2, hq=4), "SATTN_ERR_SHAPE"),              # per-head masks must number Hq
+])
+def test_bwd_sparse_rejects(lib, kwargs, status):
+    st = _bwd_sparse(lib, **kwargs)
+    assert STATUS[st] == status, (STATUS[st], lib.sattn_last_error())
+
+
+def test_bwd_sparse_zero_size_ok(lib):
+    assert _bwd_sparse(lib, n=0, mask=0, **{x: 0 for x in BWD_PTRS}) == 0

@@ -14,7 +14,8 @@ import torch
 import workloads as W
 from exact_tiled_attention_sattn_amd import (sattn_fwd, sattn_fwd_split, sattn_merge, sattn_fwd_varlen,
                                              sattn_fwd_cache, sattn_fwd_split_cache, sattn_fwd_strided,
-                                             sattn_fwd_sparse, sattn_bwd, sattn_bwd_varlen, SattnError)
+                                             sattn_fwd_sparse, sattn_bwd, sattn_bwd_varlen, sattn_bwd_sparse,
+                                             SattnError)
 from oracle import dense
 from tests.parity import check_attention, check_o, check_lse, TOL
 
@@ -753,18 +754,23 @@ GRAD_ETA = {torch.bfloat16: 2.0 ** -134, torch.float16: 2.0 ** -25}
 GRAD_K = 4.0
 
 
-def _grad_bounds(q, k, v, do, o, scale, causal):
+def _grad_bounds(q, k, v, do, o, scale, causal, allowed=None):
     """Per-element bounds for one head, float64 numpy inputs: the relative
     part (dq, dk, dv), in units of u, and the underflow part (dq, dk, dv), in
-    units of the absolute error of one rounded P or dS element."""
+    units of the absolute error of one rounded P or dS element. ``allowed``
+    (optional) is the eligibility mask; rows without a key get P = 0."""
     n = q.shape[0]
     s = scale * (q @ k.T)
     elig = np.ones((n, n))
     if causal:
         elig = (np.arange(n)[None, :] <= np.arange(n)[:, None]).astype(np.float64)
-        s = np.where(elig > 0, s, -np.inf)
-    pm = np.exp(s - s.max(axis=1, keepdims=True))
-    pm /= pm.sum(axis=1, keepdims=True)
+    if allowed is not None:
+        elig = elig * allowed
+    s = np.where(elig > 0, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    pm = np.exp(s - np.where(np.isfinite(mx), mx, 0.0))
+    tot = pm.sum(axis=1, keepdims=True)
+    pm = np.where(tot > 0, pm / np.where(tot > 0, tot, 1.0), 0.0)
     dp = do @ v.T
     ds = pm * (dp - (pm * dp).sum(axis=1, keepdims=True))
     ddel = (np.abs(do) * np.abs(o)).sum(axis=1, keepdims=True)       # per unit roundoff
@@ -932,6 +938,71 @@ def test_backward_varlen_sequences_are_isolated_bitwise():
     for x, y in zip(a, b_):
         assert torch.equal(x[:300], y[:300]) and torch.equal(x[750:], y[750:])
         assert not torch.equal(x[300:750], y[300:750])
+
+
+BWD_SPARSE = [
+    # (B, Hq, Hkv, N, D, dtype, causal, left, right, n_global, mask (heads, bq, bk) or None)
+    (1, 4, 2, 600, 128, "bf16", True, 100, -1, 0, None),          # causal sliding window
+    (1, 2, 2, 700, 64, "fp16", True, 64, -1, 5, None),            # window + global tokens
+    (1, 2, 1, 300, 128, "bf16", False, 40, 40, 3, None),          # band, global queries and keys
+    (2, 4, 4, 512, 128, "bf16", False, -1, -1, 0, (4, 64, 64)),   # per-head block mask, empty query block
+    (1, 4, 2, 1000, 64, "fp16", True, 300, -1, 0, (1, 128, 128)),  # shared mask + causal window
+    (1, 2, 2, 333, 32, "fp16", True, 17, 2, 1, (2, 32, 64)),      # small blocks, ragged
+]
+
+
+@pytest.mark.parametrize("b,hq,hkv,n,d,dt,causal,left,right,ng,mask", BWD_SPARSE)
+def test_backward_sparse_full(b, hq, hkv, n, d, dt, causal, left, right, ng, mask):
+    _banner("backward sparse", b, hq, hkv, n, d, dt, causal, left, right, ng, mask)
+    from oracle import backward
+    q, k, v, bm = _sparse_case(b, hq, hkv, n, n, d, dt, mask, seed=9600 + n + d)
+    do = W.randn((b, hq, n, d), dt, torch.Generator().manual_seed(9601 + n))
+    scale = W.scale_f32(d)
+    bq, bk = (mask[1], mask[2]) if mask else (64, 64)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    bmd = None if bm is None else bm.to(DEV)
+    o, lse = sattn_fwd_sparse(qd, kd, vd, causal=causal, window=(left, right), n_global=ng, block_mask=bmd,
+                              block_q=bq, block_k=bk, scale=scale)
+    nan = float("nan")
+    dq, dk, dv = (torch.full_like(x, nan) for x in (qd, kd, vd))
+    sattn_bwd_sparse(qd, kd, vd, o, dod, lse, causal=causal, window=(left, right), n_global=ng, block_mask=bmd,
+                     block_q=bq, block_k=bk, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    bmn = None if bm is None else bm.numpy()
+    refs = backward.attention_backward_sparse_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), scale,
+                                                   causal, left, right, ng,
+                                                   bmn[0] if bmn is not None and bmn.shape[0] == 1 else bmn, bq, bk)
+    qf, kf, vf, dof, of = (W.to_f64(x.cpu()) for x in (q, k, v, do, o))
+    grp = hq // hkv
+    rel = [np.zeros(x.shape) for x in (qf, kf, vf)]
+    und = [np.zeros(x.shape) for x in (qf, kf, vf)]
+    for h in range(hq):
+        mh = None if bmn is None else (bmn[h] if bmn.shape[0] > 1 else bmn[0])
+        allowed = dense.sparse_eligibility(n, n, causal, left, right, ng, mh, bq, bk).astype(np.float64)
+        g = h // grp
+        for bi in range(b):
+            r3, a3 = _grad_bounds(qf[bi, h], kf[bi, g], vf[bi, g], dof[bi, h], of[bi, h], scale, False, allowed)
+            for dst, src in ((rel, r3), (und, a3)):
+                dst[0][bi, h] = src[0]
+                dst[1][bi, g] += src[1]
+                dst[2][bi, g] += src[2]
+    for i, (name, gr, r) in enumerate(zip(("dq", "dk", "dv"), (dq, dk, dv), refs)):
+        _check_grad(gr, r, rel[i], und[i], W.DTYPES[dt], "sparse " + name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_sparse_unrestricted_is_dense_bitwise(causal):
+    """No window, no global token, no mask: the same tiles and sums as the
+    dense backward, so the same bits."""
+    _banner("backward sparse == dense", causal)
+    q, k, v = (x.to(DEV) for x in W.qkv((2, 4, 700, 128), (2, 2, 700, 128), "bf16", 9700))
+    do = W.randn((2, 4, 700, 128), "bf16", torch.Generator().manual_seed(9701)).to(DEV)
+    o, lse = sattn_fwd_cache(q, k, v, causal=causal)
+    a = sattn_bwd_sparse(q, k, v, o, do, lse, causal=causal)
+    b_ = sattn_bwd(q, k, v, o, do, lse, causal=causal)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b_):
+        assert torch.equal(x, y)
 
 
 def test_backward_deterministic_and_inputs_preserved():

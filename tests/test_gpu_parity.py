@@ -1101,7 +1101,11 @@ def test_all_entry_points_fill_nan_outputs_on_a_side_stream_and_preserve_inputs(
         s.synchronize()
         torch.cuda.synchronize()
         assert torch.equal(o, ref_o) and torch.equal(l, ref_l), name
-    # split partials + merge, and the backward, on the side stream
+    # split partials + merge, and the backward entry points, on the side stream
+    os_, ls_ = sattn_fwd_sparse(q, k, v, causal=True, window=(50, -1), n_global=2, block_mask=bm)
+    ov, lv = sattn_fwd_varlen(qv, kv, vv, cu, max_seqlen=200, causal=True)
+    dov = do[0].transpose(0, 1).contiguous()
+    snap += [x.clone() for x in (os_, ls_, ov, lv, dov)]
     pm = torch.full((1, 4, 300, 3), float("nan"), device=DEV)
     pl, pa = _nan_like(pm), torch.full((1, 4, 300, 3, 128), float("nan"), device=DEV)
     ref_p = sattn_fwd_split_cache(q, k, v, 128, causal=True)
@@ -1112,14 +1116,21 @@ def test_all_entry_points_fill_nan_outputs_on_a_side_stream_and_preserve_inputs(
         om, lm = sattn_merge(pm, pl, pa, torch.bfloat16, out=_nan_like(q), lse=torch.full((1, 4, 300), float("nan"),
                                                                                       device=DEV))
         grads = sattn_bwd(q, k, v, o0, do, l0, causal=True, dq=_nan_like(q), dk=_nan_like(k), dv=_nan_like(v))
+        grads_s = sattn_bwd_sparse(q, k, v, os_, do, ls_, causal=True, window=(50, -1), n_global=2, block_mask=bm,
+                                   dq=_nan_like(q), dk=_nan_like(k), dv=_nan_like(v))
+        grads_v = sattn_bwd_varlen(qv, kv, vv, ov, dov, lv, cu, max_seqlen=200, causal=True, dq=_nan_like(qv),
+                                   dk=_nan_like(kv), dv=_nan_like(vv))
     s.synchronize()
     torch.cuda.synchronize()
     for x, y in zip((pm, pl, pa), ref_p):
         assert torch.equal(x, y)
     ref_g = sattn_bwd(q, k, v, o0, do, l0, causal=True)
+    ref_s = sattn_bwd_sparse(q, k, v, os_, do, ls_, causal=True, window=(50, -1), n_global=2, block_mask=bm)
+    ref_v = sattn_bwd_varlen(qv, kv, vv, ov, dov, lv, cu, max_seqlen=200, causal=True)
     torch.cuda.synchronize()
-    for x, y in zip(grads, ref_g):
-        assert torch.equal(x, y)
+    for got, want in ((grads, ref_g), (grads_s, ref_s), (grads_v, ref_v)):
+        for x, y in zip(got, want):
+            assert torch.equal(x, y)
     assert torch.isfinite(om.float()).all() and torch.isfinite(lm).all()
-    for x, y in zip(snap, (q, k, v, do)):
+    for x, y in zip(snap, (q, k, v, do, os_, ls_, ov, lv, dov)):
         assert torch.equal(x, y)

@@ -24,14 +24,18 @@ from oracle.dense import NEG_INF
 
 
 def attention_backward(q, k, v, do, scale, causal=False, allowed=None):
-    """One head, equal lengths (causal: key j eligible for query i iff
-    j <= i). q, k, v, do: [N, D] float64. ``allowed`` [N, N] (optional)
-    restricts the eligible pairs further. Returns dq, dk, dv."""
+    """One head. q, do: [Nq, D]; k, v: [Nk, D] float64. Query i sits at
+    position i + (Nk - Nq) (equal lengths: i), and causal keeps key j iff
+    j <= that position ("Attention algorithms and data movement", lessons 04
+    and 05, bottom-right alignment). ``allowed`` [Nq, Nk] (optional) restricts
+    the eligible pairs further. Returns dq, dk, dv."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     n = q.shape[0]
     s = scale * (q @ k.T)
     if causal:
-        s = np.where(np.arange(k.shape[0])[None, :] <= np.arange(n)[:, None], s, NEG_INF)
+        # query i sits at position i + (Nk - Nq): the last Nq tokens of the keys
+        pos = np.arange(n) + (k.shape[0] - n)
+        s = np.where(np.arange(k.shape[0])[None, :] <= pos[:, None], s, NEG_INF)
     if allowed is not None:
         s = np.where(np.asarray(allowed, dtype=bool), s, NEG_INF)
     m = s.max(axis=1, keepdims=True) if s.size else np.zeros((n, 1))
@@ -119,6 +123,26 @@ def attention_backward_sparse_bhnd(q, k, v, do, scale, causal=False, left=-1, ri
         g = h // group
         for b in range(b_):
             x, y, z = attention_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, False, allowed)
+            dq[b, h] = x
+            dk[b, g] += y
+            dv[b, g] += z
+    return dq, dk, dv
+
+
+def attention_backward_cache_bhnd(q, k, v, do, scale, causal=False):
+    """q, do: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D], queries at positions
+    i + (Nk - Nq). Returns dq and dk, dv (summed over each KV head's query
+    heads in ascending order); queries with no eligible key contribute
+    nothing."""
+    b_, hq = q.shape[0], q.shape[1]
+    group = hq // k.shape[1]
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(b_):
+        for h in range(hq):
+            g = h // group
+            x, y, z = attention_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
             dq[b, h] = x
             dk[b, g] += y
             dv[b, g] += z

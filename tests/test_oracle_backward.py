@@ -176,3 +176,44 @@ def test_unrestricted_sparse_is_dense_backward():
         b = backward.attention_backward_bhnd(q, k, v, do, 0.5, causal)
         for x, y in zip(a, b):
             np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 9), (5, 17), (12, 12), (9, 4)])
+def test_cache_vs_autograd_bottom_right(nq, nk):
+    """Unequal lengths, causal with query i at position i + (Nk - Nq):
+    torch float64 autograd through SDPA with the explicit mask, grouped heads
+    repeated. Queries before the first key (Nq > Nk) have no key: autograd
+    runs on the other rows only, and those rows' dQ is exactly 0."""
+    rng = np.random.default_rng(nq * 31 + nk)
+    hq, hkv, d = 4, 2, 5
+    q, do = rng.standard_normal((1, hq, nq, d)), rng.standard_normal((1, hq, nq, d))
+    k, v = rng.standard_normal((1, hkv, nk, d)), rng.standard_normal((1, hkv, nk, d))
+    dq, dk, dv = backward.attention_backward_cache_bhnd(q, k, v, do, 0.45, True)
+    pos = np.arange(nq) + (nk - nq)
+    live = pos >= 0
+    mask = torch.from_numpy(np.arange(nk)[None, :] <= pos[live][:, None])
+    qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q[:, :, live], k, v))
+    o = F.scaled_dot_product_attention(qt, kt.repeat_interleave(2, 1), vt.repeat_interleave(2, 1),
+                                       attn_mask=mask, scale=0.45)
+    o.backward(torch.from_numpy(do[:, :, live].copy()))
+    np.testing.assert_allclose(dq[:, :, live], qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    assert np.all(dq[:, :, ~live] == 0.0)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_cache_noncausal_and_equal_lengths_reduce_to_dense():
+    rng = np.random.default_rng(44)
+    q, do = rng.standard_normal((1, 2, 7, 3)), rng.standard_normal((1, 2, 7, 3))
+    k, v = rng.standard_normal((1, 2, 7, 3)), rng.standard_normal((1, 2, 7, 3))
+    for causal in (False, True):
+        a = backward.attention_backward_cache_bhnd(q, k, v, do, 0.5, causal)
+        b = backward.attention_backward_bhnd(q, k, v, do, 0.5, causal)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+    k2, v2 = rng.standard_normal((1, 2, 11, 3)), rng.standard_normal((1, 2, 11, 3))
+    dq, dk, dv = backward.attention_backward_cache_bhnd(q, k2, v2, do, 0.5, False)
+    qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k2, v2))
+    F.scaled_dot_product_attention(qt, kt, vt, scale=0.5).backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-11, atol=1e-12)

@@ -311,7 +311,18 @@ def _backward_checks(bmod):
         o.backward(torch.from_numpy(do))
         return all(np.allclose(a, t.grad.numpy(), rtol=1e-10, atol=1e-11) for a, t in ((dq, qt), (dk, kt), (dv, vt)))
 
-    for name, fn in (("autograd", autograd), ("grouped", grouped), ("varlen", varlen), ("sparse", sparse)):
+    def cache():
+        rng = np.random.default_rng(13)
+        q, do = (rng.standard_normal((1, 2, 4, 3)) for _ in range(2))
+        k, v = (rng.standard_normal((1, 2, 9, 3)) for _ in range(2))
+        dq, dk, dv = bmod.attention_backward_cache_bhnd(q, k, v, do, 0.5, True)
+        mask = torch.from_numpy(np.arange(9)[None, :] <= (np.arange(4) + 5)[:, None])
+        qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+        F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=0.5).backward(torch.from_numpy(do))
+        return all(np.allclose(a, t.grad.numpy(), rtol=1e-10, atol=1e-11) for a, t in ((dq, qt), (dk, kt), (dv, vt)))
+
+    for name, fn in (("autograd", autograd), ("grouped", grouped), ("varlen", varlen), ("sparse", sparse),
+                     ("cache", cache)):
         try:
             ok = bool(fn())
         except Exception:
@@ -324,7 +335,8 @@ BACKWARD_MUTANTS = [
     ("dK without transpose", "dk = scale * (ds.T @ q)", "dk = scale * (ds @ q)"),
     ("dQ scale dropped", "dq = scale * (ds @ k)", "dq = (ds @ k)"),
     ("dV without transpose", "dv = p.T @ do", "dv = p @ do"),
-    ("causal mask dropped in backward", "    if causal:\n        s = np.where(", "    if False:\n        s = np.where("),
+    ("causal mask dropped in backward", "    if causal:\n        # query i sits", "    if False:\n        # query i sits"),
+    ("cache positions top-left in backward", "pos = np.arange(n) + (k.shape[0] - n)", "pos = np.arange(n)"),
     ("grouped gradients overwritten, not summed", "dk[b, g] += bk", "dk[b, g] = bk"),
     ("varlen KV gradients overwritten, not summed", "dk[a:b, g] += y", "dk[a:b, g] = y"),
     ("varlen KV head taken as h % Hkv", "            g = h // group\n            x, y, z = attention_backward(q[a:b, h]",

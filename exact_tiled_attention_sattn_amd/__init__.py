@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen", "sattn_fwd_cache",
-    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse", "sattn_bwd", "sattn_bwd_varlen", "sattn_bwd_sparse",
+    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse", "sattn_bwd", "sattn_bwd_cache", "sattn_bwd_varlen", "sattn_bwd_sparse",
     "SattnError", "library", "LIB_PATH", "STATUS",
 ]
 
@@ -76,6 +76,9 @@ def library():
     lib.sattn_bwd_varlen.restype = i32
     lib.sattn_bwd_varlen.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                      i64, i32, ctypes.c_float, vp]
+    lib.sattn_bwd_cache.restype = i32
+    lib.sattn_bwd_cache.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32,
+                                    ctypes.c_float, vp]
     lib.sattn_bwd_sparse.restype = i32
     lib.sattn_bwd_sparse.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
                                      i64, i64, i64, vp, i64, i64, i64, ctypes.c_float, vp]
@@ -514,4 +517,35 @@ def sattn_bwd_sparse(q, k, v, o, dout, lse, causal=False, window=(-1, -1), n_glo
                                     _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, n, d,
                                     int(bool(causal)), int(left), int(right), int(n_global), _ptr(block_mask),
                                     heads, int(block_q), int(block_k), _scale(scale, d), _stream(dev)))
+    return dq, dk, dv
+
+
+def sattn_bwd_cache(q, k, v, o, dout, lse, causal=False, scale=None, dq=None, dk=None, dv=None, delta=None):
+    """Gradients of sum(dout * o) for o, lse = sattn_fwd_cache(q, k, v):
+    q, o, dout [B,Hq,Nq,D]; k, v [B,Hkv,Nk,D] (query i at position
+    i + Nk - Nq); lse [B,Hq,Nq] float32; ``delta`` a float32 [B,Hq,Nq]
+    workspace.
+
+    Returns (dq, dk, dv) in q's dtype."""
+    lib = library()
+    b, hq, nq, d, hkv, nk = _cache_shapes(q, k, v)
+    for t, name in ((o, "o"), (dout, "dout")):
+        _dev_tensor(t, name, q.dtype, 4)
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o/dout must match q")
+    _dev_tensor(lse, "lse", torch.float32, 3)
+    if lse.shape != (b, hq, nq):
+        raise ValueError("lse must be [B, Hq, Nq]")
+    dev = _same_device(q, k, v, o, dout, lse, dq, dk, dv, delta)
+    dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q.dtype, 4)
+    dk = torch.empty_like(k) if dk is None else _dev_tensor(dk, "dk", q.dtype, 4)
+    dv = torch.empty_like(v) if dv is None else _dev_tensor(dv, "dv", q.dtype, 4)
+    delta = torch.empty((b, hq, nq), dtype=torch.float32, device=dev) if delta is None else \
+        _dev_tensor(delta, "delta", torch.float32, 3)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape or delta.shape != (b, hq, nq):
+        raise ValueError("gradient/workspace shape mismatch")
+    with torch.cuda.device(dev):
+        _check(lib.sattn_bwd_cache(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                   _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, nq, nk, d,
+                                   int(bool(causal)), _scale(scale, d), _stream(dev)))
     return dq, dk, dv

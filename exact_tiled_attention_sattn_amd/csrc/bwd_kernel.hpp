@@ -36,6 +36,8 @@ struct BwdParams {
   uint16_t* dk;         // [B, Hkv, N, D]
   uint16_t* dv;
   int hq, hkv, n;
+  int nk, off;          // dense layout: keys per slice and the position of query 0
+                        // (Nk - Nq: queries are the last Nq tokens; 0 for equal lengths)
   int nqt;              // dQ kernel: 128-query tiles per head (varlen: per longest sequence)
   int nkt;              // dK/dV kernel: 128-key tiles per KV head (varlen: per longest sequence)
   // varlen: q, o, dout, dq are [T, Hq, D] and k, v, dk, dv [T, Hkv, D]
@@ -119,7 +121,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   // sequence, then query tile, then the query heads of the group, as in the
   // varlen forward. Offsets in elements: qbase is row q_pos0 of q/o/dout/dq,
   // kvbase key 0 of k/v, lbase row q_pos0 of lse/Delta.
-  int len, q_pos0, qh;
+  // len: queries of the slice; klen: its keys; off: position of query 0
+  int len, klen, off = 0, q_pos0, qh;
   int64_t qbase, kvbase, lbase, q_rs, kv_rs;
   if constexpr (LAYOUT == BWD_VARLEN) {
     const int grp = p.hq / p.hkv;
@@ -137,6 +140,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     a = min(max(a, 0), p.total);
     e = min(max(e, a), p.total);
     len = e - a;
+    klen = len;
     q_pos0 = qt * BM;
     if (q_pos0 >= len) return;  // uniform over the workgroup
     q_rs = (int64_t)p.hq * D;
@@ -152,11 +156,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     const int kvs = b * p.hkv + h / (p.hq / p.hkv);
     qh = h;
     len = p.n;
+    klen = p.nk;
+    off = p.off;
     q_pos0 = qt * BM;
     q_rs = D;
     kv_rs = D;
     qbase = ((int64_t)slice * p.n + q_pos0) * D;
-    kvbase = (int64_t)kvs * p.n * D;
+    kvbase = (int64_t)kvs * p.nk * D;
     lbase = (int64_t)slice * p.n + q_pos0;
   }
   const int nq = min(BM, len - q_pos0);
@@ -166,9 +172,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
   const int l32 = lane & 31, hf = lane >> 5;
   const int qrow = wave * 32 + l32;
   const bool row_ok = qrow < nq;
-  const int my_pos = q_pos0 + qrow;
+  const int my_pos = q_pos0 + off + qrow;
   const bool wave_active = wave * 32 < nq;
-  const int wave_last_pos = q_pos0 + wave * 32 + 31;
+  const int wave_last_pos = q_pos0 + off + wave * 32 + 31;
 
   // this lane's query row: Q and dO as MFMA B operands; Delta = dO . O
   u32x4 qreg[KK], dreg[KK];
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  const int k_end = CAUSAL ? min(len, q_pos0 + BM) : len;
+  const int k_end = CAUSAL ? min(klen, max(0, q_pos0 + off + BM)) : klen;
   const int ntiles = (k_end + BN - 1) / BN;
   const uint32_t row_bytes = (uint32_t)kv_rs * 2u;
   const __amdgpu_buffer_rsrc_t rk =
@@ -246,12 +252,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
     if (idx + 1 < nsteps) issue_tile(tile_of(idx + 1), nxt);
     const int kt0 = tile_of(idx) * BN;
     if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
-    bool edge = kt0 + BN > len || (CAUSAL && kt0 + BN - 1 > q_pos0 + wave * 32);
+    bool edge = kt0 + BN > klen || (CAUSAL && kt0 + BN - 1 > q_pos0 + off + wave * 32);
     if constexpr (LAYOUT == BWD_SPARSE) {
       // the wave's 32 rows lie in one mask row block and the tile's keys in
       // one key block (block_q % 32 == 0, block_k % 64 == 0)
       const int i0 = q_pos0 + wave_u * 32, i1 = min(i0 + 31, len - 1);
-      const int j1 = min(kt0 + BN, len) - 1;
+      const int j1 = min(kt0 + BN, klen) - 1;
       if (!sparse_bit(p, qh, i0, kt0) || !sparse_any(p, i0, i1, kt0, j1)) return;
       edge = edge || !sparse_all(p, i0, i1, kt0, j1);
     }
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
         float pr = fast_exp2(fmaf(s[kb][r], p.c, -lse2));
         if (edge) {
           const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= len || (CAUSAL && key > my_pos) || (LAYOUT == BWD_SPARSE && !sparse_pair(p, my_pos, key)))
+          if (key >= klen || (CAUSAL && key > my_pos) || (LAYOUT == BWD_SPARSE && !sparse_pair(p, my_pos, key)))
             pr = 0.f;
         }
         s[kb][r] = pr * (dp[kb][r] - delta);
@@ -342,7 +348,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   // tiles of query head hh start at qhead(hh) in q/dout and at lhead(hh) in
   // lse/Delta.
   const int grp = p.hq / p.hkv;
-  int len, k0, g, tok0 = 0, bq = 0;
+  // len: keys of the slice; qlen: its queries; off: position of query 0
+  int len, qlen, off = 0, k0, g, tok0 = 0, bq = 0;
   int64_t kvbase, q_rs, kv_rs;
   if constexpr (VARLEN) {
     const int lin = xcd_linear(blockIdx.x);
@@ -354,6 +361,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     a = min(max(a, 0), p.total);
     e = min(max(e, a), p.total);
     len = e - a;
+    qlen = len;
     tok0 = a;
     k0 = kt * BNK;
     if (k0 >= len) return;  // uniform over the workgroup
@@ -366,11 +374,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const int kt = lin % p.nkt;
     bq = kvs / p.hkv;
     g = kvs % p.hkv;
-    len = p.n;
+    len = p.nk;
+    qlen = p.n;
+    off = p.off;
     k0 = kt * BNK;
     q_rs = D;
     kv_rs = D;
-    kvbase = ((int64_t)kvs * p.n + k0) * D;
+    kvbase = ((int64_t)kvs * p.nk + k0) * D;
   }
   auto qhead = [&](int hh) -> int64_t {
     return VARLEN ? (int64_t)tok0 * q_rs + (int64_t)hh * D : ((int64_t)bq * p.hq + hh) * p.n * D;
@@ -412,8 +422,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   // k0; under the sparse operator (no global key among the keys) only the
   // tiles of global queries [t_begin, t_begin + npre) and then the window
   // band from band0
-  const int t_begin = CAUSAL ? k0 / BMQ : 0;
-  const int nqt = (len + BMQ - 1) / BMQ;
+  const int t_begin = CAUSAL ? max(0, k0 - off) / BMQ : 0;
+  const int nqt = (qlen + BMQ - 1) / BMQ;
   int per_head = nqt - t_begin, npre = 0, band0 = t_begin;
   if constexpr (SPARSE) {
     if (k0 >= p.n_global) {
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     const int hh = g * grp + it / per_head;
     const int t = qtile_of(it % per_head);
     const int q0 = t * BMQ;
-    const int rows = min(BMQ, len - q0);
+    const int rows = min(BMQ, qlen - q0);
     const int64_t qoff = qhead(hh) + (int64_t)q0 * q_rs;
     const int64_t loff = lhead(hh) + q0;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -514,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       float x = fast_exp2(fmaf(s[r], p.c, -lse4[r >> 2][r & 3] * kLog2e));
       if (edge) {
         const int qi = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (qi >= len || (CAUSAL && my_key > qi) || (SPARSE && !sparse_pair(p, qi, my_key))) x = 0.f;
+        if (qi >= qlen || (CAUSAL && my_key > qi + off) || (SPARSE && !sparse_pair(p, qi, my_key))) x = 0.f;
       }
       pr[r] = x;
       ds[r] = x * (dp[r] - del4[r >> 2][r & 3]);
@@ -555,11 +565,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // keys (one mask row block, one key block)
     const int wkey1 = min(wave_first_key + 31, len - 1);
     auto blk_need = [&](int qb0) {
-      return qb0 < len && sparse_bit(p, hh, qb0, wave_first_key) &&
-             sparse_any(p, qb0, min(qb0 + 31, len - 1), wave_first_key, wkey1);
+      return qb0 < qlen && sparse_bit(p, hh, qb0, wave_first_key) &&
+             sparse_any(p, qb0, min(qb0 + 31, qlen - 1), wave_first_key, wkey1);
     };
     auto blk_full = [&](int qb0) {
-      return blk_need(qb0) && sparse_all(p, qb0, min(qb0 + 31, len - 1), wave_first_key, wkey1);
+      return blk_need(qb0) && sparse_all(p, qb0, min(qb0 + 31, qlen - 1), wave_first_key, wkey1);
     };
     const uint16_t* sQ = cur;
     const uint16_t* sD = cur + TILE;
@@ -569,7 +579,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     // the wave need no mask: one branch-free body in which the second
     // block's S/dP products overlap the first block's exps, and the first
     // block's dV/dK products the second block's.
-    if (q0 + BMQ <= len && (!CAUSAL || q0 >= wave_first_key + 31) && (!SPARSE || (blk_full(q0) && blk_full(q0 + 32)))) {
+    if (q0 + BMQ <= qlen && (!CAUSAL || q0 + off >= wave_first_key + 31) &&
+        (!SPARSE || (blk_full(q0) && blk_full(q0 + 32)))) {
       static_assert(BMQ == 64, "the unmasked body takes two 32-query blocks");
       f32x16 s0, dp0, s1, dp1;
       u32x4 pb0[2], sb0[2], pb1[2], sb1[2];
@@ -604,13 +615,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < BMQ / 32; ++qb) {
       const int qb0 = q0 + qb * 32;
-      if (CAUSAL && qb0 + 31 < wave_first_key) continue;   // every query of the block precedes the wave's keys
+      if (CAUSAL && qb0 + off + 31 < wave_first_key) continue;   // every query of the block precedes the wave's keys
       if (SPARSE && !blk_need(qb0)) continue;
       f32x16 s, dp;
       u32x4 pb[2], sb[2];
       sd_mfma(sQ, sD, qb, s, dp);
       probs(sL, sE, qb, s, dp, pb, sb,
-            qb0 + 32 > len || (CAUSAL && qb0 < wave_first_key + 31) || (SPARSE && !blk_full(qb0)), qb0);
+            qb0 + 32 > qlen || (CAUSAL && qb0 + off < wave_first_key + 31) || (SPARSE && !blk_full(qb0)), qb0);
       dvdk_mfma(sQ, sD, qb, pb, sb);
     }
   };

@@ -154,10 +154,12 @@ template <class E, int D, int LAYOUT>
 void launch_bwd(const BwdParams& p, bool causal, int64_t grid_q, int64_t grid_kv, hipStream_t s) {
   if (causal) {
     hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, LAYOUT>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+    if (grid_kv > 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, LAYOUT>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+    if (grid_kv > 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
   }
 }
 
@@ -484,22 +486,26 @@ int sattn_fwd_sparse(int dtype, const void* q, const void* k, const void* v, voi
   return cache_impl(dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, D, qs, ks, causal, scale, stream, &sp);
 }
 
+// Backward on [B, H, N, D] slices: Nq queries at positions i + (Nk - Nq)
+// against Nk keys (Nq = Nk for sattn_bwd and the sparse operator).
 static int bwd_impl(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq,
-                    int64_t Hkv, int64_t N, int64_t D, int causal, float scale, void* stream,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, void* stream,
                     const SparseSpec* sp = nullptr) {
   int st = check_common(dtype, D, scale);
   if (st) return st;
-  if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return fail(SATTN_ERR_SHAPE, "negative size");
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return fail(SATTN_ERR_SHAPE, "negative size");
   if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return fail(SATTN_ERR_SHAPE, "Hq must be a multiple of Hkv");
   int64_t qrows, kvrows, qbytes, kvbytes;
-  if (!product({B, Hq, N}, &qrows) || !product({B, Hkv, N}, &kvrows) || !product({qrows, D, 2}, &qbytes) ||
+  if (!product({B, Hq, Nq}, &qrows) || !product({B, Hkv, Nk}, &kvrows) || !product({qrows, D, 2}, &qbytes) ||
       !product({kvrows, D, 2}, &kvbytes))
     return fail(SATTN_ERR_SHAPE, "size overflow");
   if (qrows == 0) return ok();
-  if (N >= kMaxLen || B * Hq >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "size too large");
-  if (N * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
-  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return fail(SATTN_ERR_NULL, "null pointer");
+  if (Nq >= kMaxLen || Nk >= kMaxLen || B * Hq >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "size too large");
+  if (Nk * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
+  // with no key at all (Nk = 0) only dq (all zero) and delta are written
+  if (!q || !o || !dout || !lse || !delta || !dq || (kvrows > 0 && (!k || !v || !dk || !dv)))
+    return fail(SATTN_ERR_NULL, "null pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
     return fail(SATTN_ERR_ALIGN, "16-bit tensors need 16-byte, lse/delta 4-byte alignment");
@@ -513,8 +519,8 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
           sp->block_q >= kMaxLen || sp->block_k >= kMaxLen)
         return fail(SATTN_ERR_UNSUPPORTED, "block_q must be a positive multiple of 32 and block_k of 64");
       if (sp->mask_heads != 1 && sp->mask_heads != Hq) return fail(SATTN_ERR_SHAPE, "mask_heads must be 1 or Hq");
-      const int64_t nqb = (N + sp->block_q - 1) / sp->block_q;
-      nkb = (N + sp->block_k - 1) / sp->block_k;
+      const int64_t nqb = (Nq + sp->block_q - 1) / sp->block_q;
+      nkb = (Nk + sp->block_k - 1) / sp->block_k;
       if (!product({sp->mask_heads, nqb, nkb}, &mbytes)) return fail(SATTN_ERR_SHAPE, "size overflow");
     }
   }
@@ -537,9 +543,11 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
   p.dv = (uint16_t*)dv;
   p.hq = (int)Hq;
   p.hkv = (int)Hkv;
-  p.n = (int)N;
-  p.nqt = (int)((N + 127) / 128);
-  p.nkt = (int)((N + 127) / 128);
+  p.n = (int)Nq;
+  p.nk = (int)Nk;
+  p.off = (int)(Nk - Nq);
+  p.nqt = (int)((Nq + 127) / 128);
+  p.nkt = (int)((Nk + 127) / 128);
   p.c = scale * kLog2e;
   p.scale = scale;
   const int64_t grid_q = B * Hq * p.nqt, grid_kv = B * Hkv * p.nkt;
@@ -563,7 +571,13 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
 int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
               const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
               int64_t N, int64_t D, int causal, float scale, void* stream) {
-  return bwd_impl(dtype, q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale, stream);
+  return bwd_impl(dtype, q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, N, D, causal, scale, stream);
+}
+
+int sattn_bwd_cache(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, void* stream) {
+  return bwd_impl(dtype, q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, Nq, Nk, D, causal, scale, stream);
 }
 
 int sattn_bwd_sparse(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -572,7 +586,7 @@ int sattn_bwd_sparse(int dtype, const void* q, const void* k, const void* v, con
                      int64_t n_global, const uint8_t* block_mask, int64_t mask_heads, int64_t block_q,
                      int64_t block_k, float scale, void* stream) {
   const SparseSpec sp{win_left, win_right, n_global, block_mask, mask_heads, block_q, block_k};
-  return bwd_impl(dtype, q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, D, causal, scale, stream, &sp);
+  return bwd_impl(dtype, q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, N, D, causal, scale, stream, &sp);
 }
 
 int sattn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -198,6 +198,26 @@ int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void
               void* stream);
 
 /*
+ * Backward pass of sattn_fwd_cache (contiguous layouts): the same gradients
+ * as sattn_bwd for Nq queries against an Nk-key cache, query i at position
+ * i + (Nk - Nq) ("Attention algorithms and data movement", lessons 04 and
+ * 05: unequal-length alignment, cache payload).
+ *
+ *   q, o, dout, dq : [B, Hq, Nq, D];  k, v, dk, dv : [B, Hkv, Nk, D]  (dtype).
+ *   lse, delta     : [B, Hq, Nq] float32 (lse as written by sattn_fwd_cache
+ *                    for the same inputs, causal and scale; delta a
+ *                    caller-owned workspace).
+ *   causal         : nonzero -> key j eligible for query i iff
+ *                    j <= i + (Nk - Nq).
+ * Queries with no eligible key (i + Nk - Nq < 0, or Nk = 0) get dq = 0. With
+ * Nk = 0 only dq and delta are written and k, v, dk, dv may be NULL.
+ * Errors as sattn_bwd. sattn_bwd is this call with Nq = Nk.
+ */
+int sattn_bwd_cache(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq,
+                    int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, void* stream);
+
+/*
  * Backward pass of sattn_fwd_varlen: the same gradients as sattn_bwd for
  * packed variable-length sequences with grouped KV heads ("Attention
  * algorithms and data movement", lesson 04: per-sequence boundaries and

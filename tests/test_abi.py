@@ -333,3 +333,25 @@ def test_bwd_sparse_rejects(lib, kwargs, status):
 
 def test_bwd_sparse_zero_size_ok(lib):
     assert _bwd_sparse(lib, n=0, mask=0, **{x: 0 for x in BWD_PTRS}) == 0
+
+
+def _bwd_cache(lib, nq=8, nk=16, hq=2, **ptrs):
+    a = dict(BWD_PTRS)
+    a.update(ptrs)
+    return lib.sattn_bwd_cache(1, *(_bp(a[x]) for x in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv")),
+                               1, hq, 1, nq, nk, 64, 1, F32(0.125), NULL)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(nk=-1), "SATTN_ERR_SHAPE"),
+    (dict(dk=0), "SATTN_ERR_NULL"),                      # keys exist: dk needed
+    (dict(dk=0x200000 + 1024), "SATTN_ERR_ALIAS"),       # dk inside k (16 keys x 64 x 2 B = 2 KiB)
+    (dict(nk=1 << 31), "SATTN_ERR_UNSUPPORTED"),
+])
+def test_bwd_cache_rejects(lib, kwargs, status):
+    st = _bwd_cache(lib, **kwargs)
+    assert STATUS[st] == status, (STATUS[st], lib.sattn_last_error())
+
+
+def test_bwd_cache_zero_queries_ok(lib):
+    assert _bwd_cache(lib, nq=0, **{x: 0 for x in BWD_PTRS}) == 0

@@ -14,7 +14,7 @@ import torch
 import workloads as W
 from exact_tiled_attention_sattn_amd import (sattn_fwd, sattn_fwd_split, sattn_merge, sattn_fwd_varlen,
                                              sattn_fwd_cache, sattn_fwd_split_cache, sattn_fwd_strided,
-                                             sattn_fwd_sparse, sattn_bwd, sattn_bwd_varlen, sattn_bwd_sparse,
+                                             sattn_fwd_sparse, sattn_bwd, sattn_bwd_cache, sattn_bwd_varlen, sattn_bwd_sparse,
                                              SattnError)
 from oracle import dense
 from tests.parity import check_attention, check_o, check_lse, TOL
@@ -761,7 +761,7 @@ def _grad_bounds(q, k, v, do, o, scale, causal, allowed=None):
     (optional) is the eligibility mask; rows without a key get P = 0."""
     n = q.shape[0]
     s = scale * (q @ k.T)
-    elig = np.ones((n, n))
+    elig = np.ones((n, k.shape[0]))
     if causal:
         elig = (np.arange(n)[None, :] <= np.arange(n)[:, None]).astype(np.float64)
     if allowed is not None:
@@ -1003,6 +1003,73 @@ def test_backward_sparse_unrestricted_is_dense_bitwise(causal):
     torch.cuda.synchronize()
     for x, y in zip(a, b_):
         assert torch.equal(x, y)
+
+
+BWD_CACHE = [
+    # (B, Hq, Hkv, Nq, Nk, D, dtype, causal)
+    (1, 4, 2, 100, 300, 128, "bf16", True),      # chunk at the end of a longer cache
+    (1, 2, 2, 300, 100, 64, "fp16", True),       # more queries than keys: empty rows
+    (2, 4, 1, 129, 700, 128, "bf16", False),
+    (1, 2, 2, 1, 513, 64, "fp16", True),         # one decode query
+    (1, 2, 1, 257, 257, 32, "bf16", True),       # equal lengths
+]
+
+
+@pytest.mark.parametrize("b,hq,hkv,nq,nk,d,dt,causal", BWD_CACHE)
+def test_backward_cache_full(b, hq, hkv, nq, nk, d, dt, causal):
+    _banner("backward cache", b, hq, hkv, nq, nk, d, dt, causal)
+    from oracle import backward
+    q, k, v = W.qkv((b, hq, nq, d), (b, hkv, nk, d), dt, 9800 + nq + nk)
+    do = W.randn((b, hq, nq, d), dt, torch.Generator().manual_seed(9801 + nq))
+    scale = W.scale_f32(d)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = sattn_fwd_cache(qd, kd, vd, causal=causal, scale=scale)
+    nan = float("nan")
+    dq, dk, dv = (torch.full_like(x, nan) for x in (qd, kd, vd))
+    sattn_bwd_cache(qd, kd, vd, o, dod, lse, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    refs = backward.attention_backward_cache_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(do), scale,
+                                                  causal)
+    allowed = np.ones((nq, nk))
+    if causal:
+        allowed = (np.arange(nk)[None, :] <= (np.arange(nq) + nk - nq)[:, None]).astype(np.float64)
+    qf, kf, vf, dof, of = (W.to_f64(x.cpu()) for x in (q, k, v, do, o))
+    grp = hq // hkv
+    rel = [np.zeros(x.shape) for x in (qf, kf, vf)]
+    und = [np.zeros(x.shape) for x in (qf, kf, vf)]
+    for h in range(hq):
+        g = h // grp
+        for bi in range(b):
+            r3, a3 = _grad_bounds(qf[bi, h], kf[bi, g], vf[bi, g], dof[bi, h], of[bi, h], scale, False, allowed)
+            for dst, src in ((rel, r3), (und, a3)):
+                dst[0][bi, h] = src[0]
+                dst[1][bi, g] += src[1]
+                dst[2][bi, g] += src[2]
+    for i, (name, gr, r) in enumerate(zip(("dq", "dk", "dv"), (dq, dk, dv), refs)):
+        _check_grad(gr, r, rel[i], und[i], W.DTYPES[dt], "cache " + name)
+    if causal and nq > nk:
+        assert torch.all(dq[:, :, :nq - nk] == 0)
+
+
+def test_backward_cache_equal_lengths_is_dense_and_empty_cache():
+    """Nq = Nk is sattn_bwd bit for bit; an empty cache (Nk = 0) gives dq = 0
+    everywhere (and no key gradients to write)."""
+    _banner("backward cache == dense, empty cache")
+    q, k, v = (x.to(DEV) for x in W.qkv((1, 4, 500, 128), (1, 2, 500, 128), "bf16", 9900))
+    do = W.randn((1, 4, 500, 128), "bf16", torch.Generator().manual_seed(9901)).to(DEV)
+    for causal in (False, True):
+        o, lse = sattn_fwd_cache(q, k, v, causal=causal)
+        a = sattn_bwd_cache(q, k, v, o, do, lse, causal=causal)
+        b_ = sattn_bwd(q, k, v, o, do, lse, causal=causal)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b_):
+            assert torch.equal(x, y)
+    k0, v0 = k[:, :, :0], v[:, :, :0]
+    o, lse = sattn_fwd_cache(q, k0, v0, causal=True)
+    dq = torch.full_like(q, float("nan"))
+    _, dk, dv = sattn_bwd_cache(q, k0, v0, o, do, lse, causal=True, dq=dq)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
 
 
 def test_backward_deterministic_and_inputs_preserved():

@@ -106,10 +106,30 @@ struct Tile {
   static constexpr int BN = 64;
 };
 
+template <class E, int D, int NW, bool CAUSAL, int MODE>
+void launch_fwd_nw(const FwdParams& p, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_kernel<E, D, Tile<D, MODE>::BN, NW, CAUSAL, MODE>), dim3((unsigned)grid), dim3(NW * 64), 0, s,
+                     p);
+}
+
 template <class E, int D, bool CAUSAL, int MODE>
 void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t s) {
-  using T = Tile<D, MODE>;
-  hipLaunchKernelGGL((fwd_kernel<E, D, T::BN, T::NW, CAUSAL, MODE>), dim3((unsigned)grid), dim3(T::NW * 64), 0, s, p);
+  launch_fwd_nw<E, D, Tile<D, MODE>::NW, CAUSAL, MODE>(p, grid, s);
+}
+
+// Cache mode at D = 128 with long query chunks: 8 waves (256 rows) per
+// workgroup, as the dense path, so each staged K/V tile serves twice the
+// rows (2% faster on a 2048-query chunk against 16384 cached tokens); short
+// chunks keep 128-row tiles, which waste fewer rows.
+constexpr int64_t kCacheWideRows = 512;
+void dispatch_cache_wide(int dtype, bool causal, const FwdParams& p, int64_t grid, hipStream_t s) {
+  if (dtype == SATTN_BF16) {
+    if (causal) launch_fwd_nw<Bf16, 128, 8, true, MODE_CACHE>(p, grid, s);
+    else launch_fwd_nw<Bf16, 128, 8, false, MODE_CACHE>(p, grid, s);
+  } else {
+    if (causal) launch_fwd_nw<F16, 128, 8, true, MODE_CACHE>(p, grid, s);
+    else launch_fwd_nw<F16, 128, 8, false, MODE_CACHE>(p, grid, s);
+  }
 }
 
 template <int MODE>
@@ -419,7 +439,8 @@ static int cache_impl(int dtype, const void* q, const void* k, const void* v, vo
                   range_of(sp ? sp->mask : nullptr, mbytes, "block_mask")};
   Range outs[2] = {range_of(o, obytes, "o"), range_of(lse, qrows * 4, "lse")};
   if ((st = check_alias(ins, 4, outs, 2))) return st;
-  const int bm = sp ? tile_m<MODE_SPARSE>(D) : tile_m<MODE_CACHE>(D);
+  const bool wide = !sp && D == 128 && Nq >= kCacheWideRows;
+  const int bm = sp ? tile_m<MODE_SPARSE>(D) : (wide ? 256 : tile_m<MODE_CACHE>(D));
   const int64_t nqt = (Nq + bm - 1) / bm;
   const int64_t grid = B * Hq * nqt;
   if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
@@ -452,6 +473,8 @@ static int cache_impl(int dtype, const void* q, const void* k, const void* v, vo
     p.bm_nkb = (int)nkb;
     p.bm_hstride = (sp->mask && sp->mask_heads > 1) ? mbytes / sp->mask_heads : 0;
     dispatch_fwd<MODE_SPARSE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+  } else if (wide) {
+    dispatch_cache_wide(dtype, causal != 0, p, grid, (hipStream_t)stream);
   } else {
     dispatch_fwd<MODE_CACHE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
   }

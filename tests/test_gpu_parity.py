@@ -472,6 +472,9 @@ CACHE_SMALL = [
     (1, 2, 1, 200, 70, 128, "bf16"),     # more queries than cache: empty rows
     (1, 8, 2, 300, 1000, 128, "fp16"),   # several tiles both ways, 4 heads per KV head
     (1, 2, 2, 5, 0, 64, "bf16"),         # empty cache
+    # long chunks at D = 128 take 256-row workgroups
+    (1, 4, 2, 700, 1500, 128, "bf16"),   # ragged tiles, 2 heads per KV head
+    (1, 2, 1, 600, 300, 128, "fp16"),    # more queries than cache: empty rows
 ]
 
 
@@ -632,6 +635,7 @@ STRIDED = [
     ("broadcast", 3, 4, 2, 70, 190, 64, "bf16"),
     ("packed", 2, 4, 4, 333, 333, 128, "bf16"),
     ("packed", 1, 2, 2, 65, 65, 32, "fp16"),
+    ("transposed", 1, 4, 2, 600, 900, 128, "bf16"),   # a long chunk: 256-row workgroups
 ]
 
 

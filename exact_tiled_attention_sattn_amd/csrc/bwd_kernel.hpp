@@ -108,9 +108,11 @@ struct TileLoader {
 };
 
 // ---------------------------------------------------------------- dQ
-template <class E, int D, bool CAUSAL, int LAYOUT>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdParams p) {
-  constexpr int NW = 4, BM = 128, BN = 64;
+// NW waves, 32 queries each: 4, or 8 for the non-causal batched layout at
+// D = 128, where each staged K/V tile then serves twice the queries.
+template <class E, int D, bool CAUSAL, int LAYOUT, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdParams p) {
+  constexpr int BM = 32 * NW, BN = 64;
   constexpr int KK = D / 16, KB = BN / 32, DB = D / 32;
   constexpr int TILE = BN * D;  // elements of one K or V tile
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[2 * TILE];
@@ -652,8 +654,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 // Explicit instantiations: every backward kernel's host stub is emitted
 // here (implicit instantiation through the launches alone left most of them
 // undefined in the shared library).
-#define SATTN_BWD_INST2(E_, D_, C_, V_)                                      \
-  template __global__ void bwd_dq_kernel<E_, D_, C_, V_>(const BwdParams); \
+#define SATTN_BWD_INST2(E_, D_, C_, V_)                                         \
+  template __global__ void bwd_dq_kernel<E_, D_, C_, V_, 4>(const BwdParams); \
   template __global__ void bwd_dkdv_kernel<E_, D_, C_, V_>(const BwdParams);
 #define SATTN_BWD_INST(E_, D_, C_) \
   SATTN_BWD_INST2(E_, D_, C_, BWD_DENSE) SATTN_BWD_INST2(E_, D_, C_, BWD_VARLEN) SATTN_BWD_INST2(E_, D_, C_, BWD_SPARSE)
@@ -661,6 +663,8 @@ SATTN_BWD_INST(Bf16, 32, false) SATTN_BWD_INST(Bf16, 32, true) SATTN_BWD_INST(Bf
 SATTN_BWD_INST(Bf16, 64, true) SATTN_BWD_INST(Bf16, 128, false) SATTN_BWD_INST(Bf16, 128, true)
 SATTN_BWD_INST(F16, 32, false) SATTN_BWD_INST(F16, 32, true) SATTN_BWD_INST(F16, 64, false)
 SATTN_BWD_INST(F16, 64, true) SATTN_BWD_INST(F16, 128, false) SATTN_BWD_INST(F16, 128, true)
+template __global__ void bwd_dq_kernel<Bf16, 128, false, BWD_DENSE, 8>(const BwdParams);
+template __global__ void bwd_dq_kernel<F16, 128, false, BWD_DENSE, 8>(const BwdParams);
 #undef SATTN_BWD_INST
 #undef SATTN_BWD_INST2
 

@@ -169,15 +169,23 @@ void dispatch_split(int dtype, int64_t D, const FwdParams& p, int64_t grid, hipS
   }
 }
 
+// Waves of the dQ kernel: 8 (256 queries per workgroup) for the non-causal
+// batched layout at D = 128, else 4 (8 measured 4% faster non-causal and 6%
+// slower causal on the batched workload).
+constexpr int bwd_dq_waves(int D, bool causal, int layout) {
+  return (D == 128 && !causal && layout == BWD_DENSE) ? 8 : 4;
+}
+
 // dQ first: it also writes Delta, which the dK/dV kernel reads (stream order).
 template <class E, int D, int LAYOUT>
 void launch_bwd(const BwdParams& p, bool causal, int64_t grid_q, int64_t grid_kv, hipStream_t s) {
   if (causal) {
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, LAYOUT>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, LAYOUT, 4>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
     if (grid_kv > 0)
       hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, LAYOUT>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
+    constexpr int NWQ = bwd_dq_waves(D, false, LAYOUT);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, LAYOUT, NWQ>), dim3((unsigned)grid_q), dim3(NWQ * 64), 0, s, p);
     if (grid_kv > 0)
       hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
   }
@@ -569,11 +577,12 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
   p.n = (int)Nq;
   p.nk = (int)Nk;
   p.off = (int)(Nk - Nq);
-  p.nqt = (int)((Nq + 127) / 128);
+  const int64_t bmq = 32 * bwd_dq_waves((int)D, causal != 0, sp ? BWD_SPARSE : BWD_DENSE);
+  p.nqt = (int)((Nq + bmq - 1) / bmq);
   p.nkt = (int)((Nk + 127) / 128);
   p.c = scale * kLog2e;
   p.scale = scale;
-  const int64_t grid_q = B * Hq * p.nqt, grid_kv = B * Hkv * p.nkt;
+  const int64_t grid_q = B * Hq * p.nqt, grid_kv = B * Hkv * p.nkt;  // dQ: BM = bmq rows per workgroup
   if (grid_q >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
   if (sp) {
     p.win_left = (int)sp->left;

@@ -119,8 +119,9 @@ void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t s) {
 
 // Cache mode at D = 128 with long query chunks: 8 waves (256 rows) per
 // workgroup, as the dense path, so each staged K/V tile serves twice the
-// rows (2% faster on a 2048-query chunk against 16384 cached tokens); short
-// chunks keep 128-row tiles, which waste fewer rows.
+// rows (2% faster on a 2048-query chunk against 16384 cached tokens, 3-6%
+// non-causal at Nq = Nk = 4096); short chunks keep 128-row tiles, which
+// waste fewer rows.
 constexpr int64_t kCacheWideRows = 512;
 void dispatch_cache_wide(int dtype, bool causal, const FwdParams& p, int64_t grid, hipStream_t s) {
   if (dtype == SATTN_BF16) {
@@ -447,7 +448,9 @@ static int cache_impl(int dtype, const void* q, const void* k, const void* v, vo
                   range_of(sp ? sp->mask : nullptr, mbytes, "block_mask")};
   Range outs[2] = {range_of(o, obytes, "o"), range_of(lse, qrows * 4, "lse")};
   if ((st = check_alias(ins, 4, outs, 2))) return st;
-  const bool wide = !sp && D == 128 && Nq >= kCacheWideRows;
+  // causal with Nk < 2 Nq: the diagonal makes 256-row tiles uneven (9% slower
+  // at Nq = Nk = 4096), so only non-causal calls and prefill-like chunks
+  const bool wide = !sp && D == 128 && Nq >= kCacheWideRows && (!causal || Nk >= 2 * Nq);
   const int bm = sp ? tile_m<MODE_SPARSE>(D) : (wide ? 256 : tile_m<MODE_CACHE>(D));
   const int64_t nqt = (Nq + bm - 1) / bm;
   const int64_t grid = B * Hq * nqt;

@@ -429,8 +429,11 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   //    exceeds 2^64 (or is not finite) raises `overflow`; if any row of the
   //    workgroup did, the workgroup recomputes its rows with the exact online
   //    update (a data-dependent slow path; random inputs never take it).
+  //    For fp16 the limit is 2^15 instead: each p is rounded to fp16 for the
+  //    PV product, whose largest finite value is 65504, and a tile sum <= 2^15
+  //    bounds every p in it.
   bool overflow = false;
-  constexpr float FAST_LIMIT = 18446744073709551616.0f;  // 2^64
+  constexpr float FAST_LIMIT = E::kFastLimit;
 
   // One tile: wait for its loads, start the next tile's loads into the other
   // buffer, then compute on this one.

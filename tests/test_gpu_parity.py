@@ -401,19 +401,37 @@ def _growth_inputs(n, d, dt, jump, seed):
     return q, k, v
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("jump", [3.0, 50.0])
-def test_score_growth_after_first_tile(causal, jump):
-    """jump 3: scores grow by ~2^49 in exp2 units (absorbed by the fixed
-    reference); jump 50: the tile sums overflow and the workgroup takes the
-    exact online update instead. Both must match the oracle."""
-    _banner("growth", causal, jump)
+@pytest.mark.parametrize("jump", [0.25, 3.0, 50.0])
+def test_score_growth_after_first_tile(dt, causal, jump):
+    """Scores grow after the first key tile by sqrt(D)*jump*scale: jump 0.25
+    is 2^4 in exp2 units (absorbed by the fixed reference in both dtypes);
+    jump 3 is 2^49, absorbed for bf16 but past the fp16 range of the rounded
+    P, so fp16 takes the exact online update; jump 50: the tile sums overflow
+    and both take it. All must match the oracle."""
+    _banner("growth", dt, causal, jump)
     n, d = 300, 128
-    q, k, v = _growth_inputs(n, d, "bf16", jump, seed=21)
+    q, k, v = _growth_inputs(n, d, dt, jump, seed=21)
     scale = W.scale_f32(d)
     o, lse = _run_fwd(q, k, v, causal, scale)
     o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
-    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "growth")
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "growth")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_logits_fp16_streaming_kernel(causal):
+    """The large-logit variant (Q x 16, score spread ~16) on an fp16 shape
+    that takes the streaming kernel (more than 256 workgroups of 32 rows):
+    later tiles exceed the first tile's max by far more than the fp16 range
+    of the rounded P allows under the fixed reference."""
+    _banner("large logits fp16", causal)
+    q, k, v = _dense_inputs(1, 16, 1024, 64, "fp16", seed=23, qmul=16.0)
+    scale = W.scale_f32(64)
+    o, lse = _run_fwd(q, k, v, causal, scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, torch.float16, "large logits fp16")
 
 
 # Many heads at D = 128 (more query tiles than CUs, so a CU runs several

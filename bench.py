@@ -217,9 +217,47 @@ def decode_extra(steps):
            "end_to_end_GBps": total_bytes / (ms_split + ms_merge) / 1e6,
            "split_frac_of_hbm_peak": split_bytes / ms_split / 1e6 / PEAK_HBM_GBS,
            "algorithmic_bytes_split": split_bytes, "algorithmic_bytes_merge": merge_bytes}
+    out["chunk_sweep"] = chunk_sweep(q, k, v, scale, o, lse, steps)
     del q, k, v
     torch.cuda.empty_cache()
     return out
+
+
+def chunk_sweep(q, k, v, scale, o_ref, lse_ref, steps):
+    """Split width against end-to-end decode bandwidth (split + merge) on the
+    same resident K/V: narrow chunks launch more workgroups and write more
+    partials, wide ones leave CUs idle. Each width's output is checked
+    against the 4096-wide result (both lie within the bf16 tolerance of the
+    exact value, so they differ by at most twice it)."""
+    from exact_tiled_attention_sattn_amd import sattn_fwd_split, sattn_merge
+    b, hq, _, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    kv_bytes = 2 * b * hkv * nk * d * 2
+    res = []
+    for chunk in (1024, 2048, 4096, 8192, 16384, 32768, 131072):
+        c = -(-nk // chunk)
+        pm = torch.empty((b, hq, 1, c), dtype=torch.float32, device=DEV)
+        pl = torch.empty_like(pm)
+        pa = torch.empty((b, hq, 1, c, d), dtype=torch.float32, device=DEV)
+        o = torch.empty_like(o_ref)
+        lse = torch.empty_like(lse_ref)
+
+        def both():
+            sattn_fwd_split(q, k, v, chunk, scale, part_m=pm, part_l=pl, part_acc=pa)
+            sattn_merge(pm, pl, pa, torch.bfloat16, out=o, lse=lse)
+        both()
+        torch.cuda.synchronize()
+        err = (o.float() - o_ref.float()).abs()
+        if not bool((err <= 2e-2 + 2e-2 * o_ref.float().abs()).all()) or \
+                float((lse - lse_ref).abs().max()) > 2e-3:
+            raise RuntimeError("chunk sweep: chunk %d disagrees with the 4096-wide result" % chunk)
+        t = float(np.mean(time_launches(both, steps, 2)))
+        part_bytes = b * hq * c * (d + 2) * 4
+        total = kv_bytes + 2 * part_bytes + b * hq * d * 2 * 2 + b * hq * 4
+        res.append({"chunk": chunk, "partials_per_row": c, "split_workgroups": b * hq * c, "ms": t,
+                    "end_to_end_GBps": total / t / 1e6})
+        del pm, pl, pa
+    return res
 
 
 def varlen_extra(steps):

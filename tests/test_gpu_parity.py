@@ -464,21 +464,49 @@ def test_many_heads_with_rerun_heads(h, n, causal):
     check_attention(o[:, hs.to(DEV)].cpu(), lse[:, hs.to(DEV)].cpu(), o_ref, lse_ref, torch.bfloat16, "many heads")
 
 
-def test_score_growth_varlen_fallback():
-    _banner("growth varlen")
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("jump", [3.0, 50.0])
+def test_score_growth_varlen_fallback(dt, jump):
+    """The first sequence's scores grow after its first key tile: by 2^49 in
+    exp2 units (jump 3: the fixed reference for bf16, the exact update for
+    fp16) or far past the tile-sum limit (jump 50: the exact update)."""
+    _banner("growth varlen", dt, jump)
     lengths = [200, 130]
     t = sum(lengths)
     g = torch.Generator().manual_seed(22)
-    q = torch.ones((t, 4, 128), dtype=torch.bfloat16)
+    q = torch.ones((t, 4, 128), dtype=W.DTYPES[dt])
     k = torch.zeros((t, 2, 128), dtype=torch.float32)
-    k[64:200] = 50.0            # first sequence: huge growth after its first tile
-    k = k.to(torch.bfloat16)
-    v = torch.randn((t, 2, 128), generator=g).to(torch.bfloat16)
+    k[64:200] = jump
+    k = k.to(W.DTYPES[dt])
+    v = torch.randn((t, 2, 128), generator=g).to(W.DTYPES[dt])
     cu = W.cu_seqlens_of(lengths)
     o, lse = sattn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(cu), causal=True)
     torch.cuda.synchronize()
     o_ref, lse_ref = dense.varlen_gqa(W.to_f64(q), W.to_f64(k), W.to_f64(v), cu, W.scale_f32(128), True)
-    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "growth varlen")
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "growth varlen")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq", [100, 600])
+def test_score_growth_cache(dt, causal, nq):
+    """Queries against a cache whose keys after the first tile raise every
+    score by 2^49 in exp2 units: fp16 must leave the fixed reference (its
+    rounded P would overflow), bf16 keeps it. 600 queries take the 256-row
+    workgroups."""
+    _banner("growth cache", dt, causal, nq)
+    nk, d = 700, 128
+    g = torch.Generator().manual_seed(24)
+    q = torch.ones((1, 4, nq, d), dtype=W.DTYPES[dt])
+    k = torch.zeros((1, 2, nk, d), dtype=torch.float32)
+    k[:, :, 64:] = 3.0
+    k = k.to(W.DTYPES[dt])
+    v = torch.randn((1, 2, nk, d), generator=g).to(W.DTYPES[dt])
+    scale = W.scale_f32(d)
+    o, lse = sattn_fwd_cache(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.attention_cache(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, W.DTYPES[dt], "growth cache")
 
 
 # ------------------------------------------------- queries against a K/V cache

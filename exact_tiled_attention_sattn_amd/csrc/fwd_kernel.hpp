@@ -428,7 +428,8 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   //    acc <= 2^110 for any N < 2^30 and |v| < 2^16. A row whose tile sum
   //    exceeds 2^64 (or is not finite) raises `overflow`; if any row of the
   //    workgroup did, the workgroup recomputes its rows with the exact online
-  //    update (a data-dependent slow path; random inputs never take it).
+  //    update (a data-dependent slow path; random inputs never take it), as
+  //    does a workgroup whose acc is not finite after the pass.
   //    For fp16 the limit is 2^15 instead: each p is rounded to fp16 for the
   //    PV product, whose largest finite value is 65504, and a tile sum <= 2^15
   //    bounds every p in it.
@@ -665,7 +666,18 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
     run(no);  // the partial state exports the exact chunk max
   } else {
     run(yes);
-    if (__syncthreads_or(overflow ? 1 : 0)) {  // rare: redo with the exact update
+    // The tile-sum limit bounds acc only for |v| < 2^16; a numerator that
+    // overflowed fp32 (huge values under a large score growth) also takes
+    // the exact update.
+    // (a sum of magnitudes is inf or NaN iff some element is, or the sum
+    // itself overflows, which also means huge values)
+    float asum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asum[r & 3] += fabsf(acc[db][r]);
+    const bool acc_bad = !((asum[0] + asum[1]) + (asum[2] + asum[3]) <= 3.402823466e38f);
+    if (__syncthreads_or((overflow || acc_bad) ? 1 : 0)) {  // rare: redo with the exact update
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll

@@ -420,6 +420,25 @@ def test_score_growth_after_first_tile(dt, causal, jump):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_huge_values_under_score_growth(causal):
+    """bf16 values of magnitude ~1e25 with every score growing by 2^50 after
+    the first key tile: the tile sums stay under the fixed-reference limit,
+    but p*v would overflow the fp32 numerator; the workgroup must take the
+    exact update and return the finite result."""
+    _banner("huge values", causal)
+    n, d = 300, 128
+    q, k, v = _growth_inputs(n, d, "bf16", 3.0625, seed=25)
+    # positive values: a causal row that sees two keys of opposite sign would
+    # otherwise test the cancellation of 1e25-sized terms, not the fallback
+    v = ((v.float().abs() + 0.5) * 1e25).to(torch.bfloat16)
+    scale = W.scale_f32(d)
+    o, lse = _run_fwd(q, k, v, causal, scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "huge values")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_large_logits_fp16_streaming_kernel(causal):
     """The large-logit variant (Q x 16, score spread ~16) on an fp16 shape
     that takes the streaming kernel (more than 256 workgroups of 32 rows):

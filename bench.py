@@ -182,8 +182,10 @@ def small_latency(fwd, n, d, dtype_name, seed, causal, qmul=1.0):
             "event_us_median": float(np.median(ev)), "graph_samples_us": gr, "event_samples_us": ev}
 
 
-def decode_extra(steps):
-    """Split-KV decode B=16, Hq=Hkv=32, Nk=131072, D=128, chunks of 4096."""
+def decode_extra(steps, host_rows=None):
+    """Split-KV decode B=16, Hq=Hkv=32, Nk=131072, D=128, chunks of 4096.
+    ``host_rows`` (a dict, when the CPU leg runs) receives host copies of two
+    rows' q, K and V slices and the time of those device-to-host copies."""
     from exact_tiled_attention_sattn_amd import sattn_fwd_split, sattn_merge
     cfg = W.WORKLOADS["splitkv_decode_16x32x131072x128_bf16"]
     b, hq, hkv, nk, d, chunk = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["Nk"], cfg["D"], cfg["chunk"]
@@ -225,6 +227,13 @@ def decode_extra(steps):
            "split_frac_of_hbm_peak": split_bytes / ms_split / 1e6 / PEAK_HBM_GBS,
            "algorithmic_bytes_split": split_bytes, "algorithmic_bytes_merge": merge_bytes}
     out["chunk_sweep"] = chunk_sweep(q, k, v, scale, o, lse, steps)
+    if host_rows is not None:
+        for flat in (0, 511):
+            bb, h = divmod(flat, hq)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            qs, ks, vs = q[bb, h].cpu(), k[bb, h].cpu(), v[bb, h].cpu()
+            host_rows[flat] = (qs, ks, vs, time.perf_counter() - t0)
     del q, k, v
     torch.cuda.empty_cache()
     return out
@@ -594,6 +603,76 @@ def cpu_baseline(budget_s):
             "host_cores_visible": len(os.sched_getaffinity(0)), "cpu_model": cpu_model}
 
 
+def cpu_oracle_per_workload(decode_rows, budget_rows_varlen=64):
+    """The FP64 oracle on each workload, timed on the host cores: the two
+    small shapes in full (median of 5), the decode on the rows copied to the
+    host (per row, and the device-to-host time of their slices), the packed
+    varlen workload on seeded rows per (sequence, query head), scaled to the
+    full workload by FLOPs and labelled as an estimate."""
+    from oracle import dense
+
+    def med_ms(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append((time.perf_counter() - t0) * 1e3)
+        return float(np.median(ts)), ts
+
+    out = {}
+    q, k, v = W.qkv((1, 1, 129, 32), (1, 1, 129, 32), "fp16", W.WORKLOADS["single_head_129x32_fp16_causal"]["seed"])
+    qh, kh, vh = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    sc = W.scale_f32(32)
+    m, ts = med_ms(lambda: dense.attention_bhnd(qh, kh, vh, sc, True))
+    out["129x32_fp16_causal"] = {"oracle_ms_median": m, "oracle_ms_samples": ts, "rows": "all 129"}
+    q, k, v = W.qkv((1, 1, 512, 64), (1, 1, 512, 64), "fp16", W.WORKLOADS["single_head_512x64_fp16"]["seed"])
+    kh, vh = W.to_f64(k), W.to_f64(v)
+    sc = W.scale_f32(64)
+    for qmul in (1.0, 16.0):
+        qh = W.to_f64(q) * qmul
+        for causal in (True, False):
+            m, ts = med_ms(lambda: dense.attention_bhnd(qh, kh, vh, sc, causal))
+            out["512x64_fp16_%s%s" % ("causal" if causal else "noncausal", "_q16" if qmul != 1.0 else "")] = {
+                "oracle_ms_median": m, "oracle_ms_samples": ts, "rows": "all 512"}
+    if decode_rows:
+        sc = W.scale_f32(128)
+        per_row, d2h = [], []
+        for flat, (qs, ks, vs, t_copy) in sorted(decode_rows.items()):
+            qd, kd, vd = W.to_f64(qs), W.to_f64(ks), W.to_f64(vs)
+            t0 = time.perf_counter()
+            dense.attention(qd, kd, vd, sc, False)
+            per_row.append((time.perf_counter() - t0) * 1e3)
+            d2h.append(t_copy * 1e3)
+        out["splitkv_decode_16x32x131072x128_bf16"] = {
+            "oracle_ms_per_row": per_row, "rows": sorted(decode_rows),
+            "d2h_ms_per_row_slice": d2h, "d2h_bytes_per_row_slice": 2 * 131072 * 128 * 2 + 128 * 2,
+            "estimate_all_512_rows_s": float(np.mean(per_row)) * 512 / 1e3,
+            "note": "estimate = mean per-row oracle time x 512 rows, D2H excluded"}
+    cfg = W.WORKLOADS["varlen_gqa_8seq_32q8kv_128_bf16_causal"]
+    lengths = W.varlen_lengths(cfg["seed"], cfg["S"], cfg["max_len"])
+    hq, hkv, d = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    t = int(lengths.sum())
+    q, k, v = W.qkv((t, hq, d), (t, hkv, d), "bf16", cfg["seed"])
+    qh, kh, vh = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    cu = W.cu_seqlens_of(lengths)
+    rows, flop_s = {}, 0.0
+    for si, L in enumerate(lengths):
+        for h in range(hq):
+            r = W.sample_rows(2000 + si * hq + h, int(L), min(budget_rows_varlen, int(L)))[0]
+            rows[(si, h)] = r
+            flop_s += float(np.sum(4.0 * (r + 1) * d))     # QK^T and PV over the eligible keys
+    t0 = time.perf_counter()
+    dense.varlen_gqa(qh, kh, vh, cu, W.scale_f32(d), True, rows=rows)
+    el = time.perf_counter() - t0
+    flop_full = float(sum(2 * int(L) * int(L) * d * hq for L in lengths))
+    out["varlen_gqa_8seq_32q8kv_128_bf16_causal"] = {
+        "oracle_s": el, "rows": "%d seeded rows per (sequence, query head), %d in all" % (
+            budget_rows_varlen, sum(len(r) for r in rows.values())),
+        "oracle_TFLOPs": flop_s / el / 1e12, "estimate_full_s": flop_full / (flop_s / el),
+        "note": "estimate = the workload's FLOPs at the sampled rows' rate"}
+    return out
+
+
 def load_traffic(src_hash, launch_bytes):
     """HBM traffic of the dominant kernel from the committed counter summary,
     only if it was taken on the current kernel sources."""
@@ -699,6 +778,7 @@ def main():
                 "kernel": "fwd_kernel<Bf16, D=128, BN=64, 8 waves, noncausal, dense>",
                 "algorithmic_flop_per_launch": f_nc,
                 "launch_ms_mean": float(np.mean(ms_nc))}
+    decode_rows = {}   # host copies of decode rows for the CPU leg
     extras = {"noncausal_TFLOPs": tf_nc, "causal_TFLOPs": tf_c,
               "noncausal_frac_of_bf16_peak": tf_nc / PEAK_BF16_TFLOPS,
               "causal_frac_of_bf16_peak": tf_c / PEAK_BF16_TFLOPS,
@@ -714,7 +794,8 @@ def main():
         extras["latency_512x64_fp16_noncausal"] = small_latency(sattn_fwd, 512, 64, "fp16", 2, False)
         extras["latency_129x32_fp16_causal"] = small_latency(sattn_fwd, 129, 32, "fp16", 1, True)
         log("split-KV decode")
-        extras["splitkv_decode"] = decode_extra(max(3, min(args.steps, 10)))
+        extras["splitkv_decode"] = decode_extra(max(3, min(args.steps, 10)),
+                                                host_rows=None if args.no_cpu_baseline else decode_rows)
         log("varlen GQA")
         extras["varlen_gqa"] = varlen_extra(max(3, min(args.steps, 10)))
         log("chunked prefill against a K/V cache")
@@ -735,6 +816,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(args.cpu_budget_s)
+        log("cpu oracle per workload")
+        cpu["per_workload"] = cpu_oracle_per_workload(decode_rows)
     line = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",

@@ -319,16 +319,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdParams p) {
     }
     if (t < nsteps) step(t, sbuf0, sbuf1);
   }
-  if (!row_ok) return;
-  uint16_t* op = p.dq + qbase + (int64_t)qrow * q_rs;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hf;
-      *(u32x2*)(op + d) = u32x2{E::pack2(acc[db][g4 * 4 + 0] * p.scale, acc[db][g4 * 4 + 1] * p.scale),
-                                E::pack2(acc[db][g4 * 4 + 2] * p.scale, acc[db][g4 * 4 + 3] * p.scale)};
-    }
+  // dQ leaves through the idle tile buffers as whole rows (waves 0-3 in
+  // sbuf0, 4-7 in sbuf1), once every wave is done with them
+  __syncthreads();
+  store_tile_rows<E, D>(acc, p.scale, (wave_u < 4 ? sbuf0 : sbuf1) + (wave_u & 3) * 32 * D,
+                        p.dq + qbase + (int64_t)wave_u * 32 * q_rs, q_rs, nq - wave_u * 32);
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -636,19 +631,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     }
     if (it < nsteps) step(it, sbuf0, sbuf1);
   }
-  if (!key_ok) return;
-  uint16_t* kp = p.dk + kvbase + (int64_t)krow * kv_rs;
-  uint16_t* vp = p.dv + kvbase + (int64_t)krow * kv_rs;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + 8 * g4 + 4 * hf;
-      *(u32x2*)(kp + d) = u32x2{E::pack2(adk[db][g4 * 4 + 0] * p.scale, adk[db][g4 * 4 + 1] * p.scale),
-                                E::pack2(adk[db][g4 * 4 + 2] * p.scale, adk[db][g4 * 4 + 3] * p.scale)};
-      *(u32x2*)(vp + d) = u32x2{E::pack2(adv[db][g4 * 4 + 0], adv[db][g4 * 4 + 1]),
-                                E::pack2(adv[db][g4 * 4 + 2], adv[db][g4 * 4 + 3])};
-    }
+  // dK and dV leave through the idle buffers as whole rows (dK in sbuf0,
+  // dV in sbuf1, a 32-row slice per wave), once every wave is done with them
+  __syncthreads();
+  store_tile_rows<E, D>(adk, p.scale, sbuf0 + wave_u * 32 * D, p.dk + kvbase + (int64_t)wave_u * 32 * kv_rs, kv_rs,
+                        nkeys - wave_u * 32);
+  store_tile_rows<E, D>(adv, 1.0f, sbuf1 + wave_u * 32 * D, p.dv + kvbase + (int64_t)wave_u * 32 * kv_rs, kv_rs,
+                        nkeys - wave_u * 32);
 }
 
 // Explicit instantiations: every backward kernel's host stub is emitted

@@ -72,4 +72,43 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
 // Value of `x` held by lane (lane ^ 32).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
+// Writes a wave's 32 x D output tile, held in the 32x32x16 MFMA accumulator
+// layout (lane l owns row l % 32; acc[db][4*g4 + e] is column
+// db*32 + 8*g4 + 4*(l / 32) + e), times `mul`, rounded once, as whole rows.
+// Stored straight from that layout, one instruction would write 8 bytes into
+// each of 32 rows (32 partial cache lines). Instead the wave writes its rows
+// into its own LDS slice `st` (32 * D elements; 16-byte chunk c of row r at
+// chunk c ^ (r mod D/8), which spreads a column of chunks over the banks),
+// then stores 16-byte lanes covering 64 / (D/8) whole rows per instruction,
+// nontemporal. Row r (only r < rows) goes to dst + r * rs. The caller makes
+// sure no other wave still reads `st`.
+template <class E, int D>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], float mul, uint16_t* st,
+                                                uint16_t* dst, int64_t rs, int rows) {
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  int lane = threadIdx.x & 63;
+  // the lane-dependent offsets are formed here, not hoisted into the
+  // caller's main loop, where they would hold registers for its whole walk
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c = db * 4 + g4;
+      const u32x2 v = {E::pack2(acc[db][g4 * 4 + 0] * mul, acc[db][g4 * 4 + 1] * mul),
+                       E::pack2(acc[db][g4 * 4 + 2] * mul, acc[db][g4 * 4 + 3] * mul)};
+      *(u32x2*)(st + l32 * D + ((c ^ (l32 & (CPR - 1))) * 8) + 4 * hf) = v;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's rows are in LDS
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int r = it * RPI + lane / CPR;
+    const int c = lane % CPR;
+    const u32x4 val = *(const u32x4*)(st + r * D + ((c ^ (r & (CPR - 1))) * 8));
+    if (r < rows) __builtin_nontemporal_store(val, (u32x4*)(dst + (int64_t)r * rs + c * 8));
+  }
+}
+
 }  // namespace sattn

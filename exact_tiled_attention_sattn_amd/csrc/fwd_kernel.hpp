@@ -695,40 +695,10 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   if constexpr (MODE != MODE_SPLIT) {
     // an empty row (no eligible key) gives O = 0 and lse = -inf
     const float inv = (EMPTY_ROWS && lt == 0.f) ? 0.f : 1.f / lt;
-    // O leaves through LDS: in the accumulator layout a store instruction
-    // would write 8 bytes into each of 32 rows (32 partial cache lines), so
-    // each wave first writes its 32 rows to its own slice of the idle tile
-    // buffers (16-byte chunk c of row r at chunk c ^ (r mod CPR), which
-    // spreads a column of chunks over the banks), then stores whole rows
-    // with 16-byte lanes: 64/CPR rows, 1 KiB contiguous per row group.
-    constexpr int CPR = D / 8;           // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;        // rows per store instruction
-    uint16_t* st = (wave_u < 4 ? sbuf0 : sbuf1) + (wave_u & 3) * 32 * D;
-    // lane-dependent offsets are formed here, not hoisted into the tile loop
-    // (where they would hold registers for the whole walk)
-    int wrow = l32;
-    int rlane = lane;
-    asm volatile("" : "+v"(wrow), "+v"(rlane));
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int c = db * 4 + g4;       // chunk of d = db*32 + 8*g4 .. +7; this lane holds half of it
-        const u32x2 outv = {E::pack2(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv),
-                            E::pack2(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
-        *(u32x2*)(st + wrow * D + ((c ^ (wrow & (CPR - 1))) * 8) + 4 * hf) = outv;
-      }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's rows are in LDS
-    const int rows_here = w.nq - wave_u * 32;              // valid rows of this wave (>= 1)
-#pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int r = it * RPI + rlane / CPR;
-      const int c = rlane % CPR;
-      const u32x4 val = *(const u32x4*)(st + r * D + ((c ^ (r & (CPR - 1))) * 8));
-      // nontemporal: O is not read again here, and its lines would otherwise
-      // take L2 space from the K/V tiles other workgroups of the head still read
-      if (r < rows_here) __builtin_nontemporal_store(val, (u32x4*)(w.o + (int64_t)(wave_u * 32 + r) * w.o_rs + c * 8));
-    }
+    // O leaves through LDS (the idle tile buffers), as whole rows: waves 0-3
+    // use slices of sbuf0, waves 4-7 of sbuf1
+    store_tile_rows<E, D>(acc, inv, (wave_u < 4 ? sbuf0 : sbuf1) + (wave_u & 3) * 32 * D,
+                          w.o + (int64_t)wave_u * 32 * w.o_rs, w.o_rs, w.nq - wave_u * 32);
     if (row_ok && hf == 0) w.lse[qrow] = (m + fast_log2(lt)) * kLn2;
   } else {
     if (!row_ok) return;

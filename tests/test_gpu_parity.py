@@ -1270,3 +1270,70 @@ def test_all_entry_points_fill_nan_outputs_on_a_side_stream_and_preserve_inputs(
     assert torch.isfinite(om.float()).all() and torch.isfinite(lm).all()
     for x, y in zip(snap, (q, k, v, do, os_, ls_, ov, lv, dov)):
         assert torch.equal(x, y)
+
+
+# ------------------------------------------- outputs written only in bounds
+def _guarded(shape, dtype, guard=4096):
+    """A contiguous tensor of `shape` inside a NaN-filled buffer with `guard`
+    elements before and after it (offsets keep 16-byte alignment)."""
+    n = int(np.prod(shape))
+    buf = torch.full((guard + n + guard,), float("nan"), dtype=dtype, device=DEV)
+    return buf, buf[guard:guard + n].view(shape), guard
+
+
+def _guards_intact(buf, guard, n):
+    head, tail = buf[:guard], buf[guard + n:]
+    return bool(torch.isnan(head.float()).all()) and bool(torch.isnan(tail.float()).all())
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_outputs_stay_in_bounds(dt, causal):
+    """Every forward layout and the backward stage their output rows through
+    LDS and store whole rows: with ragged row counts (partial waves and
+    workgroups), nothing may be written before or after the output tensors,
+    and the results still match the oracle."""
+    _banner("guards", dt, causal)
+    dtype = W.DTYPES[dt]
+    # batched: 300 rows, D = 128 (256-row workgroups, a 44-row tail)
+    b, h, n, d = 1, 3, 300, 128
+    q, k, v = _dense_inputs(b, h, n, d, dt, seed=31)
+    scale = W.scale_f32(d)
+    ob, o, g = _guarded((b, h, n, d), dtype)
+    lb, lse, gl = _guarded((b, h, n), torch.float32)
+    sattn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert _guards_intact(ob, g, o.numel()) and _guards_intact(lb, gl, lse.numel())
+    o_ref, lse_ref = dense.attention_bhnd(W.to_f64(q), W.to_f64(k), W.to_f64(v), scale, causal)
+    check_attention(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype, "guards dense")
+    # backward of the same call: dq, dk, dv with 300 rows / keys
+    do = W.randn((b, h, n, d), dt, torch.Generator().manual_seed(32))
+    gbufs = [_guarded((b, h, n, d), dtype) for _ in range(3)]
+    sattn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), o, do.to(DEV), lse, causal=causal, scale=scale,
+              dq=gbufs[0][1], dk=gbufs[1][1], dv=gbufs[2][1])
+    torch.cuda.synchronize()
+    for (bb, t, gg) in gbufs:
+        assert _guards_intact(bb, gg, t.numel())
+        assert torch.isfinite(t.float()).all()
+    # packed varlen: ragged sequences, 4 query heads on 2 KV heads, D = 64
+    lengths = [37, 130, 5]
+    q2, k2, v2, cu = _varlen_inputs(lengths, 4, 2, 64, dt, seed=33)
+    t_ = sum(lengths)
+    ob2, o2, g2 = _guarded((t_, 4, 64), dtype)
+    lb2, lse2, gl2 = _guarded((4, t_), torch.float32)
+    sattn_fwd_varlen(q2.to(DEV), k2.to(DEV), v2.to(DEV), torch.from_numpy(cu), causal=causal, out=o2, lse=lse2)
+    torch.cuda.synchronize()
+    assert _guards_intact(ob2, g2, o2.numel()) and _guards_intact(lb2, gl2, lse2.numel())
+    o2_ref, lse2_ref = dense.varlen_gqa(W.to_f64(q2), W.to_f64(k2), W.to_f64(v2), cu, W.scale_f32(64), causal)
+    check_attention(o2.cpu(), lse2.cpu(), o2_ref, lse2_ref, dtype, "guards varlen")
+    # queries against a cache: 600 queries (256-row workgroups when non-causal), D = 32 tails elsewhere
+    for (nq, nk, dd) in ((600, 900, 128), (45, 200, 32)):
+        q3, k3, v3 = W.qkv((1, 4, nq, dd), (1, 2, nk, dd), dt, 34)
+        ob3, o3, g3 = _guarded((1, 4, nq, dd), dtype)
+        lb3, lse3, gl3 = _guarded((1, 4, nq), torch.float32)
+        sc3 = W.scale_f32(dd)
+        sattn_fwd_cache(q3.to(DEV), k3.to(DEV), v3.to(DEV), causal=causal, scale=sc3, out=o3, lse=lse3)
+        torch.cuda.synchronize()
+        assert _guards_intact(ob3, g3, o3.numel()) and _guards_intact(lb3, gl3, lse3.numel())
+        o3_ref, lse3_ref = dense.attention_cache(W.to_f64(q3), W.to_f64(k3), W.to_f64(v3), sc3, causal)
+        check_attention(o3.cpu(), lse3.cpu(), o3_ref, lse3_ref, dtype, "guards cache")

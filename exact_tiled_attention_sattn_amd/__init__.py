@@ -381,9 +381,14 @@ def check_cu_seqlens(cu, total, max_seqlen):
         raise ValueError("cu_seqlens[-1] must equal T")
 
 
-def sattn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=True, scale=None, out=None, lse=None):
+def sattn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=True, scale=None, out=None, lse=None,
+                     cu_seqlens_host=None):
     """Packed variable-length GQA forward. q [T,Hq,D], k/v [T,Hkv,D];
-    cu_seqlens int32 [S+1] (host or device; validated on a host copy).
+    cu_seqlens int32 [S+1] (host or device). The table is validated on a host
+    copy: pass ``cu_seqlens_host`` (the same offsets, on the host) to skip
+    the device-to-host copy, which otherwise synchronizes the stream; the
+    device table is then used as given (the kernel still clamps every index
+    into [0, T)).
 
     Returns (o [T,Hq,D], lse [Hq,T] float32)."""
     lib = library()
@@ -397,17 +402,7 @@ def sattn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=True, scale=No
     if k.shape != v.shape or k.shape[0] != t or k.shape[2] != d:
         raise ValueError("k/v must be [T, Hkv, D] matching q")
     hkv = k.shape[1]
-    cu_host = cu_seqlens.detach().to("cpu", torch.int64) if isinstance(cu_seqlens, torch.Tensor) else \
-        torch.as_tensor(cu_seqlens, dtype=torch.int64)
-    lengths = (cu_host[1:] - cu_host[:-1]).tolist()
-    if max_seqlen is None:
-        max_seqlen = max(lengths) if lengths else 0
-    check_cu_seqlens(cu_host.tolist(), t, max_seqlen)
-    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32 \
-            and cu_seqlens.is_contiguous() and cu_seqlens.device == dev:
-        cu_dev = cu_seqlens
-    else:
-        cu_dev = cu_host.to(torch.int32).to(dev)
+    cu_dev, max_seqlen = _cu_device(cu_seqlens, t, max_seqlen, dev, cu_seqlens_host)
     s = cu_dev.numel() - 1
     out = torch.empty_like(q) if out is None else _dev_tensor(out, "out", q.dtype, 3)
     lse = torch.empty((hq, t), dtype=torch.float32, device=dev) if lse is None else \
@@ -421,26 +416,32 @@ def sattn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=True, scale=No
     return out, lse
 
 
-def _cu_device(cu_seqlens, total, max_seqlen, dev):
+def _cu_device(cu_seqlens, total, max_seqlen, dev, cu_host=None):
     """Host-validated cu_seqlens and its int32 device copy (reused when the
-    caller already passes a contiguous int32 tensor on that device)."""
-    cu_host = cu_seqlens.detach().to("cpu", torch.int64) if isinstance(cu_seqlens, torch.Tensor) else \
-        torch.as_tensor(cu_seqlens, dtype=torch.int64)
+    caller already passes a contiguous int32 tensor on that device). The
+    host copy is ``cu_host`` when given, else copied from ``cu_seqlens``."""
+    if cu_host is None:
+        cu_host = cu_seqlens
+    cu_host = cu_host.detach().to("cpu", torch.int64) if isinstance(cu_host, torch.Tensor) else \
+        torch.as_tensor(cu_host, dtype=torch.int64)
     lengths = (cu_host[1:] - cu_host[:-1]).tolist()
     if max_seqlen is None:
         max_seqlen = max(lengths) if lengths else 0
     check_cu_seqlens(cu_host.tolist(), total, max_seqlen)
     if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32 \
             and cu_seqlens.is_contiguous() and cu_seqlens.device == dev:
+        if cu_seqlens.numel() != cu_host.numel():
+            raise ValueError("cu_seqlens and cu_seqlens_host differ in length")
         return cu_seqlens, int(max_seqlen)
     return cu_host.to(torch.int32).to(dev), int(max_seqlen)
 
 
 def sattn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen=None, causal=True, scale=None, dq=None,
-                     dk=None, dv=None, delta=None):
+                     dk=None, dv=None, delta=None, cu_seqlens_host=None):
     """Gradients of sum(dout * o) for o, lse = sattn_fwd_varlen(q, k, v,
     cu_seqlens). q, o, dout [T,Hq,D]; k, v [T,Hkv,D]; lse [Hq,T] float32;
-    ``delta`` is a float32 [Hq,T] workspace.
+    ``delta`` is a float32 [Hq,T] workspace. ``cu_seqlens_host`` as in
+    sattn_fwd_varlen.
 
     Returns (dq, dk, dv) in q's dtype."""
     lib = library()
@@ -457,7 +458,7 @@ def sattn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen=None, causal=
     if lse.shape != (hq, t_):
         raise ValueError("lse must be [Hq, T]")
     dev = _same_device(q, k, v, o, dout, lse, dq, dk, dv, delta)
-    cu_dev, max_seqlen = _cu_device(cu_seqlens, t_, max_seqlen, dev)
+    cu_dev, max_seqlen = _cu_device(cu_seqlens, t_, max_seqlen, dev, cu_seqlens_host)
     dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q.dtype, 3)
     dk = torch.empty_like(k) if dk is None else _dev_tensor(dk, "dk", q.dtype, 3)
     dv = torch.empty_like(v) if dv is None else _dev_tensor(dv, "dv", q.dtype, 3)

@@ -640,21 +640,4 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
                         nkeys - wave_u * 32);
 }
 
-// Explicit instantiations: every backward kernel's host stub is emitted
-// here (implicit instantiation through the launches alone left most of them
-// undefined in the shared library).
-#define SATTN_BWD_INST2(E_, D_, C_, V_)                                         \
-  template __global__ void bwd_dq_kernel<E_, D_, C_, V_, 4>(const BwdParams); \
-  template __global__ void bwd_dkdv_kernel<E_, D_, C_, V_>(const BwdParams);
-#define SATTN_BWD_INST(E_, D_, C_) \
-  SATTN_BWD_INST2(E_, D_, C_, BWD_DENSE) SATTN_BWD_INST2(E_, D_, C_, BWD_VARLEN) SATTN_BWD_INST2(E_, D_, C_, BWD_SPARSE)
-SATTN_BWD_INST(Bf16, 32, false) SATTN_BWD_INST(Bf16, 32, true) SATTN_BWD_INST(Bf16, 64, false)
-SATTN_BWD_INST(Bf16, 64, true) SATTN_BWD_INST(Bf16, 128, false) SATTN_BWD_INST(Bf16, 128, true)
-SATTN_BWD_INST(F16, 32, false) SATTN_BWD_INST(F16, 32, true) SATTN_BWD_INST(F16, 64, false)
-SATTN_BWD_INST(F16, 64, true) SATTN_BWD_INST(F16, 128, false) SATTN_BWD_INST(F16, 128, true)
-template __global__ void bwd_dq_kernel<Bf16, 128, false, BWD_DENSE, 8>(const BwdParams);
-template __global__ void bwd_dq_kernel<F16, 128, false, BWD_DENSE, 8>(const BwdParams);
-#undef SATTN_BWD_INST
-#undef SATTN_BWD_INST2
-
 }  // namespace sattn

@@ -25,6 +25,9 @@ struct Bf16 {
   // Largest per-tile sum of exps the fixed-reference update accepts (bf16
   // shares fp32's exponent range, so only the fp32 sums bound it).
   static constexpr float kFastLimit = 18446744073709551616.0f;  // 2^64
+  // A block past the limit raises a flag (recomputed after the walk)
+  // rather than being redone at once.
+  static constexpr bool kRedoBlocks = false;
   static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -43,6 +46,8 @@ struct Bf16 {
 struct F16 {
   // The rounded P must stay below fp16's largest finite value, 65504.
   static constexpr float kFastLimit = 32768.0f;  // 2^15
+  // Large logits reach this limit often: a block past it is redone at once.
+  static constexpr bool kRedoBlocks = true;
   static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);

@@ -41,6 +41,21 @@ enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_CACHE = 3, MODE_SPA
 // Key tiles a sparse workgroup may list (Nk <= 64 * kSparseMaxTiles).
 constexpr int kSparseMaxTiles = 1024;
 
+// Build-time knobs of the design-variant builds (the library sets none):
+// one K/V tile buffer, loaded after every wave is done with the previous
+// tile, instead of two; causal key tiles after a row's position visited and
+// masked instead of skipped.
+#ifdef SATTN_SINGLE_BUFFER
+constexpr bool kSingleBuffer = true;
+#else
+constexpr bool kSingleBuffer = false;
+#endif
+#ifdef SATTN_NO_CAUSAL_SKIP
+constexpr bool kCausalSkip = false;
+#else
+constexpr bool kCausalSkip = true;
+#endif
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -141,7 +156,7 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, int item, Work& 
     w.kv_rs = D;
     w.lse = p.lse + (int64_t)head * p.n + w.q_pos0;
     w.k_begin = 0;
-    w.k_end = CAUSAL ? min(p.n, w.q_pos0 + BM) : p.n;
+    w.k_end = (CAUSAL && kCausalSkip) ? min(p.n, w.q_pos0 + BM) : p.n;
     w.pos_mod = 0;
     return w.nq > 0;
   } else if constexpr (MODE == MODE_VARLEN) {
@@ -422,17 +437,19 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   //  * exact online update: running max, acc/l rescaled when the max grows
   //    (lazily, by more than 2^8 in exp2 units outside the split path);
   //  * fixed reference (FAST): the row's max over the first tile is kept as m
-  //    for all later tiles, which then need no max and no rescale at all:
+  //    for later tiles, which then need no max and no rescale:
   //    p = exp2(S*c - m). O and lse do not depend on which m is used as long
   //    as nothing overflows; with every tile sum <= 2^64, l <= 2^94 and
-  //    acc <= 2^110 for any N < 2^30 and |v| < 2^16. A row whose tile sum
-  //    exceeds 2^64 (or is not finite) raises `overflow`; if any row of the
-  //    workgroup did, the workgroup recomputes its rows with the exact online
-  //    update (a data-dependent slow path; random inputs never take it), as
-  //    does a workgroup whose acc is not finite after the pass.
-  //    For fp16 the limit is 2^15 instead: each p is rounded to fp16 for the
-  //    PV product, whose largest finite value is 65504, and a tile sum <= 2^15
-  //    bounds every p in it.
+  //    acc <= 2^110 for any N < 2^30 and |v| < 2^16.
+  //    bf16: a tile sum past 2^64 (scores grown by 2^64 over the first
+  //    tile's max) raises `overflow`, and the workgroup recomputes its rows
+  //    with the exact update after the walk, as does a workgroup whose acc is
+  //    not finite (huge values).
+  //    fp16: the limit is 2^15, since each p is rounded to fp16 for the PV
+  //    product, whose largest finite value is 65504 (a sum <= 2^15 bounds
+  //    every p in it); large logits reach it often, so a 32-key block past it
+  //    is redone at once for its rows with the exact update (see the tile
+  //    body), which moves their reference up to the running maximum.
   bool overflow = false;
   constexpr float FAST_LIMIT = E::kFastLimit;
 
@@ -441,72 +458,85 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   // Sparse mode walks a list of the key tiles some wave needs (built below):
   // entry = tile | (waves that need it) << 16 | (element mask needed) << 24.
   int nact = 0;
-  auto step = [&](int idx, const uint16_t* cur, uint16_t* nxt, auto mask_tag, auto fast_tag) {
+  auto body = [&](int idx, int t, int e, const uint16_t* cur, auto mask_tag, auto fast_tag) {
     constexpr bool MASKED = decltype(mask_tag)::value;
     constexpr bool FAST = decltype(fast_tag)::value;
-    const int e = SPARSE ? tlist[idx] : idx;
-    const int t = SPARSE ? (e & 0xffff) : idx;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t visible to all waves; every wave is done with the previous tile
-    if (SPARSE) {
-      if (idx + 1 < nact) issue_tile(tlist[idx + 1] & 0xffff, nxt);
-    } else if (t + 1 < ntiles) {
-      issue_tile(t + 1, nxt);
-    }
-
     const int kt0 = w.k_begin + t * BN;
-    if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
+    if (!wave_active || (CAUSAL && kCausalSkip && kt0 > wave_last_pos)) return;
     if (SPARSE && !((e >> (16 + wave_u)) & 1)) return;   // this wave's query block or window skips the tile
     const uint16_t* sK = cur;
     const uint16_t* sV = cur + BN * D;
 
-    // ---- S^T = K Q^T for BN keys x 32 queries (all K operands read first)
-    u32x4 ka[KB][KK];
+    // ---- S^T = K Q^T for one 32-key block x 32 queries, then its masks:
+    // key tail, and keys after the query (diagonal kept); in sparse mode
+    // also the window / global-token rule, only on listed tiles that some
+    // row does not wholly see
+    auto score_block = [&](f32x16& sb, int kb) {
+      u32x4 ka[KK];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kk = 0; kk < KK; ++kk) ka[kk] = *(const u32x4*)(sK + kofs[kk] + kb * 32 * D);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) ka[kb][kk] = *(const u32x4*)(sK + kofs[kk] + kb * 32 * D);
-    f32x16 s[KB];
+      for (int r = 0; r < 16; ++r) sb[r] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+      for (int kk = 0; kk < KK; ++kk) sb = E::mfma32(ka[kk], qreg[kk], sb);
+      if constexpr (MASKED && !SPARSE) {
+        // only where this wave's rows see a key past the tail or after them
+        if (kt0 + BN > w.k_end || (CAUSAL && kt0 + BN - 1 > wave_first_pos))
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) s[kb] = E::mfma32(ka[kb][kk], qreg[kk], s[kb]);
-    }
-
-    // ---- mask: key tail, and keys after the query (diagonal kept); in
-    // sparse mode also the window / global-token rule, only on listed tiles
-    // that some row does not wholly see
-    if constexpr (MASKED && !SPARSE) {
-      // only where this wave's rows see a key past the tail or after them
-      if (kt0 + BN > w.k_end || (CAUSAL && kt0 + BN - 1 > wave_first_pos))
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if ((key >= w.k_end) || (CAUSAL && key > my_pos)) s[kb][r] = -INFINITY;
-        }
-    }
-    if constexpr (SPARSE) {
-      if ((e >> 24) & 1) {
-        const bool row_global = my_pos < p.n_global;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if ((key >= w.k_end) || (CAUSAL && key > my_pos)) sb[r] = -INFINITY;
+          }
+      }
+      if constexpr (SPARSE) {
+        if ((e >> 24) & 1) {
+          const bool row_global = my_pos < p.n_global;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
             const bool in_win = (p.win_left < 0 || key >= my_pos - p.win_left) &&
                                 (p.win_right < 0 || key <= my_pos + p.win_right);
             const bool ok = key < w.k_end && (!CAUSAL || key <= my_pos) && (in_win || key < p.n_global || row_global);
-            if (!ok) s[kb][r] = -INFINITY;
+            if (!ok) sb[r] = -INFINITY;
           }
+        }
       }
-    }
+    };
+    // p = exp2(S*c - reference) in place; returns the lane's sum
+    auto exps = [&](f32x16& sb) {
+      const float mref = (EMPTY_ROWS && m == -INFINITY) ? 0.f : m;
+      float rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = fast_exp2(fmaf(sb[r], c, -mref));
+        sb[r] = pv;
+        rs += pv;
+      }
+      return rs;
+    };
+    // ---- O^T += V^T P^T for one 32-key block, 16 keys per MFMA
+    auto pv_block = [&](const f32x16& sb, int kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int o8 = half * 8;
+        const u32x4 pb = {E::pack2(sb[o8 + 0], sb[o8 + 1]), E::pack2(sb[o8 + 2], sb[o8 + 3]),
+                          E::pack2(sb[o8 + 4], sb[o8 + 5]), E::pack2(sb[o8 + 6], sb[o8 + 7])};
+        const int krow = (kb * 32 + half * 16) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 a0 = lds_read_tr16(sV + vofs[0][db] + krow);
+          const u32x2 a1 = lds_read_tr16(sV + vofs[1][db] + krow);
+          acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, acc[db]);
+        }
+      }
+    };
+
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) score_block(s[kb], kb);
 
     if constexpr (FAST) {
-      // ---- fixed-reference update: exps against the row's first-tile max
+      // ---- fixed-reference update: exps against the row's reference
       if constexpr (SPARSE) {
         // A row whose first kept key comes after the first tile takes its
         // reference from the first tile that has one (its acc and l are
@@ -521,18 +551,68 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
           if (m == -INFINITY) m = mx * c;
         }
       }
-      const float mref = (EMPTY_ROWS && m == -INFINITY) ? 0.f : m;
-      float rs = 0.f;
+      if constexpr (E::kRedoBlocks) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+          float rs = exps(s[kb]);
+          if constexpr (!MASKED && !SPARSE && KB == 2 && KK == 8) {
+            if (kb == 0) {
+              // Keep the overlap of a branch-free tile inside the first of the
+              // blocks the check below creates: block 0's eight K reads, its
+              // MFMAs each with one of block 1's K reads, then block 1's MFMAs
+              // each with six VALU of block 0's exps.
+              __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS read
+              for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              }
+              for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 6, 0); // VALU incl. transcendental
+              }
+            }
+          }
+          // A lane's block sum past the limit (or not finite): some row's
+          // scores grew too far above its reference. The wave redoes this
+          // block (its K is still in LDS) with the exact update for those
+          // rows only: the row's reference moves up to its running maximum,
+          // acc and l are rescaled to it, and the exps are taken again. Other
+          // rows recompute the same scores and exps bit for bit, so a row's
+          // result never depends on the data of other rows.
+          if (__builtin_amdgcn_ballot_w64(!(rs <= FAST_LIMIT)) != 0) {
+            const bool bad = max_halves(!(rs <= FAST_LIMIT) ? 1.f : 0.f) > 0.f;   // either half of the row
+            // read K again rather than keep the first reads' registers alive
+            asm volatile("" ::: "memory");
+            score_block(s[kb], kb);
+            float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[kb][r], c, -mref));
-          s[kb][r] = pv;
-          rs += pv;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            const float m_cand = fmaxf(m, max_halves(mx) * c);
+            const bool need = bad && m_cand > m;
+            const float alpha = need ? fast_exp2(m - m_cand) : 1.0f;
+            m = need ? m_cand : m;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            rs = exps(s[kb]);
+          }
+          l += rs;
+          pv_block(s[kb], kb);
         }
-      l += rs;
-      overflow = overflow || !(rs <= FAST_LIMIT);
+      } else {
+        // No branch inside the tile: a sum past the limit only raises the
+        // workgroup's flag, and the walk is recomputed with the exact update
+        // at the end (a scores growth of 2^64 after the first tile).
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const float rs = exps(s[kb]);
+          l += rs;
+          overflow = overflow || !(rs <= FAST_LIMIT);
+          pv_block(s[kb], kb);
+        }
+      }
     } else {
       // ---- exact online update (fp32)
       float mx = -INFINITY;
@@ -555,35 +635,30 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       }
-      const float mref = (EMPTY_ROWS && m == -INFINITY) ? 0.f : m;
-      float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) l += exps(s[kb]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[kb][r], c, -mref));
-          s[kb][r] = pv;
-          rs += pv;
-        }
-      l += rs;
+      for (int kb = 0; kb < KB; ++kb) pv_block(s[kb], kb);
     }
+  };
 
-    // ---- O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int o8 = half * 8;
-        const u32x4 pb = {E::pack2(s[kb][o8 + 0], s[kb][o8 + 1]), E::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
-                          E::pack2(s[kb][o8 + 4], s[kb][o8 + 5]), E::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
-        const int krow = (kb * 32 + half * 16) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2 a0 = lds_read_tr16(sV + vofs[0][db] + krow);
-          const u32x2 a1 = lds_read_tr16(sV + vofs[1][db] + krow);
-          acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, acc[db]);
-        }
-      }
+  auto step = [&](int idx, const uint16_t* cur, uint16_t* nxt, auto mask_tag, auto fast_tag) {
+    const int e = SPARSE ? tlist[idx] : idx;
+    const int t = SPARSE ? (e & 0xffff) : idx;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t visible to all waves; every wave is done with the previous tile
+    if constexpr (kSingleBuffer) {  // every tile lives in sbuf0
+      body(idx, t, e, sbuf0, mask_tag, fast_tag);
+      __syncthreads();  // every wave is done with the one buffer
+      if (t + 1 < ntiles) issue_tile(t + 1, sbuf0);
+      return;
+    }
+    if (SPARSE) {
+      if (idx + 1 < nact) issue_tile(tlist[idx + 1] & 0xffff, nxt);
+    } else if (t + 1 < ntiles) {
+      issue_tile(t + 1, nxt);
+    }
+    body(idx, t, e, cur, mask_tag, fast_tag);
   };
 
   // Tiles [0, n_full) need no mask for any row of the workgroup (they end
@@ -725,8 +800,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
   // Double-buffered K and V tiles, as two distinct arrays so the compiler can
   // tell that reads of one buffer never alias the prefetch into the other
   // (otherwise it makes every LDS read wait for the in-flight prefetch).
-  __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[2 * BN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[2 * BN * D];
+  // Each buffer also stages the output rows of up to 4 waves in the
+  // epilogue (32 rows of D each), which 64-key tiles fill exactly.
+  constexpr int SBUF = (2 * BN * D > 128 * D) ? 2 * BN * D : 128 * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[SBUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[SBUF];
   __shared__ int tlist[MODE == MODE_SPARSE ? kSparseMaxTiles : 1];
   __shared__ int tcount;
   constexpr int NITEMS = items_per_block<CAUSAL, MODE>();

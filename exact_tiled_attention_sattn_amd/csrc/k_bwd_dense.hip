@@ -1,0 +1,47 @@
+// Backward kernels (dQ with Delta, then dK/dV) in the BWD_DENSE row layout.
+#include "launch.hpp"
+
+namespace sattn {
+
+namespace {
+template <class E, int D>
+void go(bool causal, const BwdParams& p, int64_t grid_q, int64_t grid_kv, hipStream_t s) {
+  if (causal) {
+    constexpr int NWQ = bwd_dq_waves(D, true, BWD_DENSE);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, BWD_DENSE, NWQ>), dim3((unsigned)grid_q), dim3(NWQ * 64), 0, s, p);
+    if (grid_kv > 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, BWD_DENSE>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+  } else {
+    constexpr int NWQ = bwd_dq_waves(D, false, BWD_DENSE);
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, BWD_DENSE, NWQ>), dim3((unsigned)grid_q), dim3(NWQ * 64), 0, s, p);
+    if (grid_kv > 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, BWD_DENSE>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+  }
+}
+}  // namespace
+
+// Explicit instantiations, so that every kernel of this layout has its
+// device code and host stub in this object.
+#define SATTN_INST(E_, D_)                                                                      \
+  template __global__ void bwd_dq_kernel<E_, D_, true, BWD_DENSE, bwd_dq_waves(D_, true, BWD_DENSE)>(const BwdParams);  \
+  template __global__ void bwd_dq_kernel<E_, D_, false, BWD_DENSE, bwd_dq_waves(D_, false, BWD_DENSE)>(const BwdParams); \
+  template __global__ void bwd_dkdv_kernel<E_, D_, true, BWD_DENSE>(const BwdParams);                                  \
+  template __global__ void bwd_dkdv_kernel<E_, D_, false, BWD_DENSE>(const BwdParams);
+SATTN_INST(Bf16, 32) SATTN_INST(Bf16, 64) SATTN_INST(Bf16, 128)
+SATTN_INST(F16, 32) SATTN_INST(F16, 64) SATTN_INST(F16, 128)
+#undef SATTN_INST
+
+void launch_bwd_dense(int dtype, int D, bool causal, const BwdParams& p, int64_t grid_q, int64_t grid_kv,
+                   hipStream_t s) {
+  if (dtype == 1) {
+    if (D == 32) go<Bf16, 32>(causal, p, grid_q, grid_kv, s);
+    else if (D == 64) go<Bf16, 64>(causal, p, grid_q, grid_kv, s);
+    else go<Bf16, 128>(causal, p, grid_q, grid_kv, s);
+  } else {
+    if (D == 32) go<F16, 32>(causal, p, grid_q, grid_kv, s);
+    else if (D == 64) go<F16, 64>(causal, p, grid_q, grid_kv, s);
+    else go<F16, 128>(causal, p, grid_q, grid_kv, s);
+  }
+}
+
+}  // namespace sattn

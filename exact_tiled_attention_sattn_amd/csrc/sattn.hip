@@ -9,10 +9,8 @@
 #include <cstdint>
 #include <cstdio>
 
-#include "../../include/sattn.h"
-#include "fwd_kernel.hpp"
-#include "fwd_small.hpp"
-#include "bwd_kernel.hpp"
+#include "sattn.h"
+#include "launch.hpp"
 
 namespace {
 
@@ -93,46 +91,7 @@ int launch_status() {
   return ok();
 }
 
-// ---------------------------------------------------------------- tiles
-// Query rows per workgroup (32 per wave) and keys per tile. Dense D = 128
-// runs 8 waves (256 query rows) per workgroup, one workgroup per CU: each K/V
-// tile staged in LDS then serves twice as many queries as with 4 waves, and
-// every SIMD still holds two waves. Varlen and split keep 4 waves, whose
-// 128-row granularity wastes fewer rows on short sequences and few queries.
-template <int D, int MODE>
-struct Tile {
-  static constexpr int NW = D == 128 ? (MODE == MODE_DENSE ? 8 : 4) : 2;
-  static constexpr int BM = NW * 32;
-  static constexpr int BN = 64;
-};
-
-template <class E, int D, int NW, bool CAUSAL, int MODE>
-void launch_fwd_nw(const FwdParams& p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_kernel<E, D, Tile<D, MODE>::BN, NW, CAUSAL, MODE>), dim3((unsigned)grid), dim3(NW * 64), 0, s,
-                     p);
-}
-
-template <class E, int D, bool CAUSAL, int MODE>
-void launch_fwd(const FwdParams& p, int64_t grid, hipStream_t s) {
-  launch_fwd_nw<E, D, Tile<D, MODE>::NW, CAUSAL, MODE>(p, grid, s);
-}
-
-// Cache mode at D = 128 with long query chunks: 8 waves (256 rows) per
-// workgroup, as the dense path, so each staged K/V tile serves twice the
-// rows (2% faster on a 2048-query chunk against 16384 cached tokens, 3-6%
-// non-causal at Nq = Nk = 4096); short chunks keep 128-row tiles, which
-// waste fewer rows.
-constexpr int64_t kCacheWideRows = 512;
-void dispatch_cache_wide(int dtype, bool causal, const FwdParams& p, int64_t grid, hipStream_t s) {
-  if (dtype == SATTN_BF16) {
-    if (causal) launch_fwd_nw<Bf16, 128, 8, true, MODE_CACHE>(p, grid, s);
-    else launch_fwd_nw<Bf16, 128, 8, false, MODE_CACHE>(p, grid, s);
-  } else {
-    if (causal) launch_fwd_nw<F16, 128, 8, true, MODE_CACHE>(p, grid, s);
-    else launch_fwd_nw<F16, 128, 8, false, MODE_CACHE>(p, grid, s);
-  }
-}
-
+// Query rows per workgroup of each mode of the streaming kernel.
 template <int MODE>
 int tile_m(int64_t D) {
   switch (D) {
@@ -142,69 +101,15 @@ int tile_m(int64_t D) {
   }
 }
 
-template <int MODE>
-void dispatch_fwd(int dtype, int64_t D, bool causal, const FwdParams& p, int64_t grid, hipStream_t s) {
-#define SATTN_CASE(E_, D_)                                   \
-  if (causal) launch_fwd<E_, D_, true, MODE>(p, grid, s);    \
-  else launch_fwd<E_, D_, false, MODE>(p, grid, s);
-  if (dtype == SATTN_BF16) {
-    if (D == 32) { SATTN_CASE(Bf16, 32) } else if (D == 64) { SATTN_CASE(Bf16, 64) } else { SATTN_CASE(Bf16, 128) }
-  } else {
-    if (D == 32) { SATTN_CASE(F16, 32) } else if (D == 64) { SATTN_CASE(F16, 64) } else { SATTN_CASE(F16, 128) }
-  }
-#undef SATTN_CASE
-}
-
-// Split-KV partial states over key chunks; causal chunks use the
-// bottom-right alignment (query i at position i + Nk - Nq).
-template <bool CAUSAL>
-void dispatch_split(int dtype, int64_t D, const FwdParams& p, int64_t grid, hipStream_t s) {
-  if (dtype == SATTN_BF16) {
-    if (D == 32) launch_fwd<Bf16, 32, CAUSAL, MODE_SPLIT>(p, grid, s);
-    else if (D == 64) launch_fwd<Bf16, 64, CAUSAL, MODE_SPLIT>(p, grid, s);
-    else launch_fwd<Bf16, 128, CAUSAL, MODE_SPLIT>(p, grid, s);
-  } else {
-    if (D == 32) launch_fwd<F16, 32, CAUSAL, MODE_SPLIT>(p, grid, s);
-    else if (D == 64) launch_fwd<F16, 64, CAUSAL, MODE_SPLIT>(p, grid, s);
-    else launch_fwd<F16, 128, CAUSAL, MODE_SPLIT>(p, grid, s);
-  }
-}
-
-// Waves of the dQ kernel: 8 (256 queries per workgroup) for the non-causal
-// batched layout at D = 128, else 4 (8 measured 4% faster non-causal and 6%
-// slower causal on the batched workload).
-constexpr int bwd_dq_waves(int D, bool causal, int layout) {
-  return (D == 128 && !causal && layout == BWD_DENSE) ? 8 : 4;
-}
-
-// dQ first: it also writes Delta, which the dK/dV kernel reads (stream order).
-template <class E, int D, int LAYOUT>
-void launch_bwd(const BwdParams& p, bool causal, int64_t grid_q, int64_t grid_kv, hipStream_t s) {
-  if (causal) {
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, LAYOUT, 4>), dim3((unsigned)grid_q), dim3(256), 0, s, p);
-    if (grid_kv > 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
-  } else {
-    constexpr int NWQ = bwd_dq_waves(D, false, LAYOUT);
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, LAYOUT, NWQ>), dim3((unsigned)grid_q), dim3(NWQ * 64), 0, s, p);
-    if (grid_kv > 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
-  }
-}
-
-template <int LAYOUT>
-void dispatch_bwd(int dtype, int64_t D, bool causal, const BwdParams& p, int64_t grid_q, int64_t grid_kv,
-                  hipStream_t s) {
-  if (dtype == SATTN_BF16) {
-    if (D == 32) launch_bwd<Bf16, 32, LAYOUT>(p, causal, grid_q, grid_kv, s);
-    else if (D == 64) launch_bwd<Bf16, 64, LAYOUT>(p, causal, grid_q, grid_kv, s);
-    else launch_bwd<Bf16, 128, LAYOUT>(p, causal, grid_q, grid_kv, s);
-  } else {
-    if (D == 32) launch_bwd<F16, 32, LAYOUT>(p, causal, grid_q, grid_kv, s);
-    else if (D == 64) launch_bwd<F16, 64, LAYOUT>(p, causal, grid_q, grid_kv, s);
-    else launch_bwd<F16, 128, LAYOUT>(p, causal, grid_q, grid_kv, s);
-  }
-}
+// Causal dense workgroups take a pair of query tiles (equal work per
+// workgroup) once the grid has enough tiles that pairing still leaves
+// several workgroups per CU (a build-time knob for the design-variant
+// builds; the library pairs).
+#ifdef SATTN_NO_PAIR
+constexpr bool kPairCausal = false;
+#else
+constexpr bool kPairCausal = true;
+#endif
 
 FwdParams blank_params(float scale) {
   FwdParams p{};
@@ -265,24 +170,9 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
     p.heads = (int)heads;
     p.n = (int)N;
     p.nqt = (int)nq32;
-    hipStream_t s = (hipStream_t)stream;
     // 8 waves when a query tile may see more than 4 key tiles, else 4.
     const bool wide = (N + 63) / 64 > 4;
-    const dim3 g((unsigned)(heads * nq32)), b(wide ? 512 : 256);
-#define SATTN_SMALL(E_, D_) \
-  if (wide) { \
-    if (causal) hipLaunchKernelGGL((fwd_small_kernel<E_, D_, 8, true>), g, b, 0, s, p); \
-    else hipLaunchKernelGGL((fwd_small_kernel<E_, D_, 8, false>), g, b, 0, s, p); \
-  } else { \
-    if (causal) hipLaunchKernelGGL((fwd_small_kernel<E_, D_, 4, true>), g, b, 0, s, p); \
-    else hipLaunchKernelGGL((fwd_small_kernel<E_, D_, 4, false>), g, b, 0, s, p); \
-  }
-    if (dtype == SATTN_BF16) {
-      if (D == 32) { SATTN_SMALL(Bf16, 32) } else { SATTN_SMALL(Bf16, 64) }
-    } else {
-      if (D == 32) { SATTN_SMALL(F16, 32) } else { SATTN_SMALL(F16, 64) }
-    }
-#undef SATTN_SMALL
+    launch_fwd_small(dtype, (int)D, causal != 0, wide, p, heads * nq32, (hipStream_t)stream);
     return launch_status();
   }
   const int bm = tile_m<MODE_DENSE>(D);
@@ -290,7 +180,7 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
   // Causal workgroups take a pair of query tiles (equal work per workgroup)
   // once the grid has enough tiles that pairing still leaves several
   // workgroups per CU.
-  const bool pair = causal && nqt * heads >= 1024;
+  const bool pair = kPairCausal && causal && nqt * heads >= 1024;
   const int64_t grid = (pair ? (nqt + 1) / 2 : nqt) * heads;
   if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
   FwdParams p = blank_params(scale);
@@ -303,7 +193,7 @@ int sattn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, f
   p.n = (int)N;
   p.nqt = (int)nqt;
   p.pair = pair ? 1 : 0;
-  dispatch_fwd<MODE_DENSE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+  launch_fwd_dense(dtype, (int)D, causal != 0, p, grid, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -363,8 +253,7 @@ static int split_impl(int dtype, const void* q, const void* k, const void* v, fl
   p.nqt = (int)nqt;
   p.off = (int)(Nk - Nq);
   p.pack = pack ? 1 : 0;
-  if (causal) dispatch_split<true>(dtype, D, p, grid, (hipStream_t)stream);
-  else dispatch_split<false>(dtype, D, p, grid, (hipStream_t)stream);
+  launch_fwd_split(dtype, (int)D, causal, p, grid, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -483,11 +372,9 @@ static int cache_impl(int dtype, const void* q, const void* k, const void* v, vo
     p.bm_k = (int)sp->block_k;
     p.bm_nkb = (int)nkb;
     p.bm_hstride = (sp->mask && sp->mask_heads > 1) ? mbytes / sp->mask_heads : 0;
-    dispatch_fwd<MODE_SPARSE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
-  } else if (wide) {
-    dispatch_cache_wide(dtype, causal != 0, p, grid, (hipStream_t)stream);
+    launch_fwd_sparse(dtype, (int)D, causal != 0, p, grid, (hipStream_t)stream);
   } else {
-    dispatch_fwd<MODE_CACHE>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+    launch_fwd_cache(dtype, (int)D, causal != 0, wide, p, grid, (hipStream_t)stream);
   }
   return launch_status();
 }
@@ -596,9 +483,9 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
     p.bm_k = (int)sp->block_k;
     p.bm_nkb = (int)nkb;
     p.bm_hstride = (sp->mask && sp->mask_heads > 1) ? mbytes / sp->mask_heads : 0;
-    dispatch_bwd<BWD_SPARSE>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
+    launch_bwd_sparse(dtype, (int)D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
   } else {
-    dispatch_bwd<BWD_DENSE>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
+    launch_bwd_dense(dtype, (int)D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
   }
   return launch_status();
 }
@@ -676,7 +563,7 @@ int sattn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, con
   p.total = (int)T;
   p.c = scale * kLog2e;
   p.scale = scale;
-  dispatch_bwd<BWD_VARLEN>(dtype, D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
+  launch_bwd_varlen(dtype, (int)D, causal != 0, p, grid_q, grid_kv, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -708,17 +595,7 @@ int sattn_merge(int dtype, const float* part_m, const float* part_l, const float
   if ((st = check_alias(ins, 3, outs, 2))) return st;
   const int64_t grid = (rows + 3) / 4;
   if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
-  hipStream_t s = (hipStream_t)stream;
-  const int c = (int)C;
-  uint16_t* out = (uint16_t*)o;
-#define SATTN_MERGE(E_, D_) \
-  hipLaunchKernelGGL((merge_kernel<E_, D_>), dim3((unsigned)grid), dim3(256), 0, s, part_m, part_l, part_acc, rows, c, out, lse)
-  if (dtype == SATTN_BF16) {
-    if (D == 32) SATTN_MERGE(Bf16, 32); else if (D == 64) SATTN_MERGE(Bf16, 64); else SATTN_MERGE(Bf16, 128);
-  } else {
-    if (D == 32) SATTN_MERGE(F16, 32); else if (D == 64) SATTN_MERGE(F16, 64); else SATTN_MERGE(F16, 128);
-  }
-#undef SATTN_MERGE
+  launch_merge(dtype, (int)D, part_m, part_l, part_acc, rows, (int)C, (uint16_t*)o, lse, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -761,7 +638,7 @@ int sattn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, voi
   p.nqt = (int)nqt;
   p.nseq = (int)S;
   p.total = (int)T;
-  dispatch_fwd<MODE_VARLEN>(dtype, D, causal != 0, p, grid, (hipStream_t)stream);
+  launch_fwd_varlen(dtype, (int)D, causal != 0, p, grid, (hipStream_t)stream);
   return launch_status();
 }
 

@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "sattn_fwd", "sattn_fwd_split", "sattn_merge", "sattn_fwd_varlen", "sattn_fwd_cache",
-    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse", "sattn_bwd", "sattn_bwd_cache", "sattn_bwd_varlen", "sattn_bwd_sparse",
+    "sattn_fwd_split_cache", "sattn_fwd_strided", "sattn_fwd_sparse", "sattn_bwd", "sattn_bwd_noalloc",
+    "sattn_bwd_cache", "sattn_bwd_varlen", "sattn_bwd_sparse",
     "SattnError", "library", "LIB_PATH", "STATUS",
 ]
 
@@ -73,6 +74,9 @@ def library():
     lib.sattn_bwd.restype = i32
     lib.sattn_bwd.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
                               ctypes.c_float, vp]
+    lib.sattn_bwd_noalloc.restype = i32
+    lib.sattn_bwd_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, fp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
+                                      ctypes.c_float, vp]
     lib.sattn_bwd_varlen.restype = i32
     lib.sattn_bwd_varlen.argtypes = [i32, vp, vp, vp, vp, vp, fp, fp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                      i64, i32, ctypes.c_float, vp]
@@ -258,6 +262,39 @@ def sattn_bwd(q, k, v, o, dout, lse, causal=False, scale=None, dq=None, dk=None,
         _check(lib.sattn_bwd(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                              _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, n, d, int(bool(causal)),
                              _scale(scale, d), _stream(dev)))
+    return dq, dk, dv
+
+
+def sattn_bwd_noalloc(q, k, v, o, dout, lse, causal=False, scale=None, dq=None, dk=None, dv=None):
+    """sattn_bwd with its Delta workspace in the library's fixed device array
+    (B*Hq*N <= 2^21 rows): the C call allocates nothing. Pass dq, dk, dv to
+    keep this binding from allocating them. Calls that overlap on one GPU
+    race on the shared array.
+
+    Returns (dq, dk, dv) in q's dtype."""
+    lib = library()
+    _dev_tensor(q, "q", ndim=4)
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q must be float16 or bfloat16")
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _dev_tensor(t, name, q.dtype, 4)
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (b, hkv, n, d) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q/o/dout must be [B,Hq,N,D] and k/v [B,Hkv,N,D]")
+    _dev_tensor(lse, "lse", torch.float32, 3)
+    if lse.shape != (b, hq, n):
+        raise ValueError("lse must be [B, Hq, N]")
+    dev = _same_device(q, k, v, o, dout, lse, dq, dk, dv)
+    dq = torch.empty_like(q) if dq is None else _dev_tensor(dq, "dq", q.dtype, 4)
+    dk = torch.empty_like(k) if dk is None else _dev_tensor(dk, "dk", q.dtype, 4)
+    dv = torch.empty_like(v) if dv is None else _dev_tensor(dv, "dv", q.dtype, 4)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient shape mismatch")
+    with torch.cuda.device(dev):
+        _check(lib.sattn_bwd_noalloc(_DTYPE_CODE[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                     _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), b, hq, hkv, n, d, int(bool(causal)),
+                                     _scale(scale, d), _stream(dev)))
     return dq, dk, dv
 
 

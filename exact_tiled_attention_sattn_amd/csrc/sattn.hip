@@ -8,9 +8,14 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "sattn.h"
 #include "launch.hpp"
+
+// Workspace of the allocation-free backward entry point (see
+// scratch_on_current_device below): 2^21 floats.
+static __device__ __align__(256) float scratch[int64_t(1) << 21];
 
 namespace {
 
@@ -115,6 +120,36 @@ FwdParams blank_params(float scale) {
   FwdParams p{};
   p.c = scale * kLog2e;
   return p;
+}
+
+// Scratch of the allocation-free backward entry point: the Delta rows live
+// in this file-scope device array (each GPU the library runs on holds its own
+// copy until the process ends). Host code must never pass `scratch` itself
+// to a kernel: its host-side name is only a handle; the device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kScratchFloats = sizeof(scratch) / sizeof(float);   // 8 MiB: up to 2^21 query rows
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (cached per
+// device). Returns SATTN_OK or SATTN_ERR_HIP.
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SATTN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SATTN_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(SATTN_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return SATTN_OK;
 }
 
 }  // namespace
@@ -409,10 +444,12 @@ int sattn_fwd_sparse(int dtype, const void* q, const void* k, const void* v, voi
 
 // Backward on [B, H, N, D] slices: Nq queries at positions i + (Nk - Nq)
 // against Nk keys (Nq = Nk for sattn_bwd and the sparse operator).
+// With `scratch_ws`, delta is ignored and the library's static scratch
+// array serves as the workspace (looked up after every check has passed).
 static int bwd_impl(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq,
                     int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D, int causal, float scale, void* stream,
-                    const SparseSpec* sp = nullptr) {
+                    const SparseSpec* sp = nullptr, bool scratch_ws = false) {
   int st = check_common(dtype, D, scale);
   if (st) return st;
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return fail(SATTN_ERR_SHAPE, "negative size");
@@ -425,7 +462,14 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
   if (Nq >= kMaxLen || Nk >= kMaxLen || B * Hq >= kMaxLen) return fail(SATTN_ERR_UNSUPPORTED, "size too large");
   if (Nk * D * 2 >= kMaxSpan) return fail(SATTN_ERR_UNSUPPORTED, "K/V slice larger than 2 GiB");
   // with no key at all (Nk = 0) only dq (all zero) and delta are written
-  if (!q || !o || !dout || !lse || !delta || !dq || (kvrows > 0 && (!k || !v || !dk || !dv)))
+  if (scratch_ws) {
+    if (qrows > kScratchFloats)
+      return fail(SATTN_ERR_UNSUPPORTED, "B*Hq*N = %lld query rows exceed the %lld-row static scratch of "
+                  "sattn_bwd_noalloc; use sattn_bwd with a caller-owned workspace", (long long)qrows,
+                  (long long)kScratchFloats);
+    delta = nullptr;
+  }
+  if (!q || !o || !dout || !lse || (!delta && !scratch_ws) || !dq || (kvrows > 0 && (!k || !v || !dk || !dv)))
     return fail(SATTN_ERR_NULL, "null pointer");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
@@ -449,8 +493,9 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
                   range_of(o, qbytes, "o"),       range_of(dout, qbytes, "dout"),     range_of(lse, qrows * 4, "lse"),
                   range_of(sp ? sp->mask : nullptr, mbytes, "block_mask")};
   Range outs[4] = {range_of(dq, qbytes, "dq"), range_of(dk, kvbytes, "dk"), range_of(dv, kvbytes, "dv"),
-                   range_of(delta, qrows * 4, "delta")};
+                   range_of(delta, scratch_ws ? 0 : qrows * 4, "delta")};
   if ((st = check_alias(ins, 7, outs, 4))) return st;
+  if (scratch_ws && (st = scratch_on_current_device(&delta))) return st;
   BwdParams p{};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -494,6 +539,13 @@ int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void
               const float* lse, float* delta, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
               int64_t N, int64_t D, int causal, float scale, void* stream) {
   return bwd_impl(dtype, q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, N, D, causal, scale, stream);
+}
+
+int sattn_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                      int64_t D, int causal, float scale, void* stream) {
+  return bwd_impl(dtype, q, k, v, o, dout, lse, nullptr, dq, dk, dv, B, Hq, Hkv, N, N, D, causal, scale, stream,
+                  nullptr, true);
 }
 
 int sattn_bwd_cache(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,

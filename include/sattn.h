@@ -198,6 +198,27 @@ int sattn_bwd(int dtype, const void* q, const void* k, const void* v, const void
               void* stream);
 
 /*
+ * sattn_bwd without the delta workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The [B, Hq, N] float32 rows of
+ * delta live in a fixed device array inside the library (8 MiB per GPU,
+ * held until the process ends), so B*Hq*N must be <= 2^21 query rows;
+ * larger problems return SATTN_ERR_UNSUPPORTED and enqueue nothing (use
+ * sattn_bwd). The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); on its first use on a device it looks up the
+ * array's address there (hipGetSymbolAddress, with that device current).
+ * Arguments, results and the other errors are those of sattn_bwd, which
+ * runs the same kernels: the gradients are bit-identical to sattn_bwd's.
+ * Every call on one GPU shares that GPU's array, and the dQ launch rewrites
+ * every row it needs before the dK/dV launch reads it, so nothing has to be
+ * cleared; calls that overlap on one GPU (different streams, or threads
+ * without ordering) race on the array and must not be issued.
+ */
+int sattn_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                      int64_t N, int64_t D, int causal, float scale, void* stream);
+
+/*
  * Backward pass of sattn_fwd_cache (contiguous layouts): the same gradients
  * as sattn_bwd for Nq queries against an Nk-key cache, query i at position
  * i + (Nk - Nq) ("Attention algorithms and data movement", lessons 04 and

@@ -355,3 +355,35 @@ def test_bwd_cache_rejects(lib, kwargs, status):
 
 def test_bwd_cache_zero_queries_ok(lib):
     assert _bwd_cache(lib, nq=0, **{x: 0 for x in BWD_PTRS}) == 0
+
+
+def _bwd_noalloc(lib, dtype=1, b=1, hq=2, hkv=1, n=8, d=64, **ptrs):
+    a = dict(BWD_PTRS)
+    a.update(ptrs)
+    return lib.sattn_bwd_noalloc(dtype, *(_bp(a[x]) for x in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv")),
+                                 b, hq, hkv, n, d, 1, F32(0.125), NULL)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=5), "SATTN_ERR_DTYPE"),
+    (dict(d=48), "SATTN_ERR_UNSUPPORTED"),
+    (dict(hq=3, hkv=2), "SATTN_ERR_SHAPE"),
+    (dict(n=-1), "SATTN_ERR_SHAPE"),
+    (dict(dq=0), "SATTN_ERR_NULL"),
+    (dict(dq=0x800008), "SATTN_ERR_ALIGN"),
+    (dict(dq=0x100000), "SATTN_ERR_ALIAS"),
+    # more query rows than the static scratch holds (2^21): rejected before
+    # any pointer is used or the HIP runtime is reached
+    (dict(b=64, hq=64, n=1024, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0), "SATTN_ERR_UNSUPPORTED"),
+])
+def test_bwd_noalloc_rejects(lib, kwargs, status):
+    st = _bwd_noalloc(lib, **kwargs)
+    assert STATUS[st] == status, (STATUS[st], lib.sattn_last_error())
+    if status == "SATTN_ERR_UNSUPPORTED" and kwargs.get("b") == 64:
+        assert b"static scratch" in lib.sattn_last_error()
+
+
+def test_bwd_noalloc_zero_size_ok_without_pointers(lib):
+    nulls = {x: 0 for x in BWD_PTRS}
+    assert _bwd_noalloc(lib, n=0, **nulls) == 0
+    assert _bwd_noalloc(lib, b=0, **nulls) == 0

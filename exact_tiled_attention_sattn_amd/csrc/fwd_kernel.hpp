@@ -612,6 +612,37 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
           overflow = overflow || !(rs <= FAST_LIMIT);
           pv_block(s[kb], kb);
         }
+        if constexpr (!MASKED && !SPARSE && KB == 2 && KK == 8 && DB == 4) {
+          // Order of the unmasked tile (one scheduling region), so that each
+          // LDS operand read is issued before the MFMA ahead of its own:
+          // block 0's eight K reads; block 0's S MFMAs, each with one of
+          // block 1's K reads; block 1's S MFMAs, each with six VALU of
+          // block 0's exps; the V reads of the first PV MFMA and block 0's P
+          // packing; block 0's PV MFMAs, each with the next MFMA's two V
+          // reads and six VALU of block 1's exps; block 1's P packing and PV
+          // MFMAs, V reads one MFMA ahead. Same arithmetic, same bits.
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // DS read
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU, transcendental included
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        }
       }
     } else {
       // ---- exact online update (fp32)

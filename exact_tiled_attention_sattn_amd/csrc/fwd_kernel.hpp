@@ -14,15 +14,21 @@
 //     so the row max and row sum are in-register reductions plus one exchange
 //     with lane ^ 32.
 //   * The output is formed transposed too, O^T = V^T P^T: P^T is the B
-//     operand and is taken straight from the score registers (no shuffles);
-//     V^T (A operand) is read from an LDS tile that is stored transposed
-//     ([d][key]). The output accumulator again gives each lane one query, so
-//     the rescale factor of a query never leaves its lane.
-//   * K/V tiles are fetched from HBM with 16-byte loads into registers one
-//     tile ahead (software prefetch) and written to LDS between barriers.
+//     operand and is packed straight from the score registers (no shuffles);
+//     V^T (A operand) is read from the row-major [key][d] V tile in LDS with
+//     transposing 8-byte reads (ds_read_b64_tr_b16). The output accumulator
+//     again gives each lane one query, so the rescale factor of a query never
+//     leaves its lane.
+//   * K/V tiles go from HBM straight into LDS (buffer loads with the LDS
+//     destination, no register staging), two tile buffers deep: one barrier
+//     per tile makes tile t visible and frees tile t-1's buffer, into which
+//     tile t+1 is then loaded while tile t is computed. Rows are permuted in
+//     16-byte pieces (swz below) so both operand reads are conflict free.
 //   * Causal: key tiles that start after a wave's last query are skipped, not
 //     masked; the mask (key > query, diagonal kept) runs only on tiles that
 //     straddle the diagonal or the key tail.
+//   * Dense D = 128 runs 8 waves (256 queries) per workgroup, two per SIMD,
+//     so each staged K/V tile serves 256 queries.
 #pragma once
 
 #include "common.hpp"

@@ -11,10 +11,10 @@
  * exp-sum, rescaled numerator) state, never forming the full score matrix.
  * Sources: "Intermediate and advanced extension" (workshop table, streaming
  * attention and split softmax rows; "Logic review before implementation":
- * numerator and denominator are both rescaled, causal rows include their
- * diagonal, a kernel boundary on one stream orders dependent launches);
+ * the output sum is rescaled with the exponential sum, a causal row sees the
+ * key at its own position, dependent launches are ordered by the stream);
  * "Attention algorithms and data movement", lessons 01 (merge partial states
- * by rescaled denominators, explicit empty-row contract), 03 (saved per-row
+ * by rescaled denominators, a stated result for a row with no key), 03 (saved per-row
  * normalization state = lse), 04 (packed causal eligibility by logical
  * position), 05 (GQA query-head to KV-head mapping).
  *

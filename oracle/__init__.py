@@ -22,13 +22,14 @@ Sources (pages, by title and section):
     row: mergeable (maximum, exponential sum) state with partition and
     merge-order invariance; streaming attention row: tile QK and PV with online
     rescaling, causal and noncausal) and "Logic review before implementation"
-    (empty maximum needs an explicit identity; numerator and denominator are
-    both rescaled; causal rows include their diagonal).
+    (a state with no keys yet, whose maximum is -inf, is a special case of its
+    own; the output sum is scaled together with the exponential sum; a causal
+    row sees the key at its own position).
   * "Intermediate and advanced workshop validation", "Correctness and review"
     (dense FP64 references, future-value perturbation, large-logit cases,
     explicit empty+empty identity).
   * "Attention algorithms and data movement", lessons 01 (merge normalized
-    attention without averaging tile outputs; explicit empty-row contract),
+    attention without averaging tile outputs; a stated result for a row that sees no key),
     03 (saved normalization state), 04 (packed causal eligibility from logical
     positions), 05 (GQA query-head to KV-head mapping).
 

@@ -13,8 +13,8 @@ standard one:
     lse_i  = m_i + ln(l_i)                        (natural log)
 
 Causal eligibility (equal query/key lengths): key j is eligible for the query
-at logical position p iff j <= p, so the diagonal is included ("Logic review
-before implementation": real causal rows include their diagonal). A row with
+at logical position p iff j <= p, so the diagonal is included (the key at the
+query's own position counts; "Logic review before implementation"). A row with
 no eligible key is the empty row: O = 0, lse = -inf, never NaN (lesson 01 of
 "Attention algorithms and data movement" asks for an explicit empty-row
 contract; the values 0 / -inf are the reading taken here).

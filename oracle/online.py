@@ -15,8 +15,9 @@ follows:
   row: the (maximum, exponential sum) state is mergeable and its result does
   not depend on how the row is partitioned or in which order parts merge.
 * "Intermediate and advanced extension", "Logic review before implementation":
-  the empty state's maximum is -inf and needs an explicit identity; attention
-  rescales the numerator accumulator as well as the denominator.
+  a state that has seen no key starts from a maximum of -inf, which must be
+  handled as a special case; when the maximum moves, both the running output
+  sum and the running exponential sum are scaled by the same factor.
 * "Intermediate and advanced workshop validation", review table: empty + empty
   is handled explicitly, so no NaN can appear.
 * "Attention algorithms and data movement", lesson 01: partials are combined

@@ -29,8 +29,12 @@ Other modes:
                     it traced) and prints a markdown summary of the headline
                     kernels' timed dispatches.
   --pmc-summary F W reads FETCH_SIZE (F) and WRITE_SIZE (W) counter CSVs of
-                    a bench run and writes the traffic summary
+                    two bench runs (their logs: --bench-log twice, in that
+                    order) and writes the traffic summary
                     profiles/fwd_kernel_batched_4x16x4096x128_bf16_pmc.{md,json}.
+  --sq-summary D    reads a --pmc pass over the SQ counters listed in
+                    SQ_COUNTERS (with --bench-log) and prints a markdown
+                    summary (MFMA busy of the headline and every kernel).
 """
 import argparse
 import csv
@@ -1091,6 +1095,14 @@ def _kname(name):
     return name.replace("sattn::", "").replace(" ", "")
 
 
+def _disp(name):
+    """A kernel name for the summaries' tables: no namespace, return type or
+    parameter list."""
+    n = name.replace("sattn::", "")
+    n = n[5:] if n.startswith("void ") else n
+    return n.split("(")[0].replace("|", "/")[:110]
+
+
 def _dispatches(per, key):
     """(dispatch id, value) of every kernel whose name contains ``key``."""
     k_ = _kname(key)
@@ -1151,27 +1163,102 @@ def trace_summary(trace_dir, bench_log, command):
             "| kernel | dispatches | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
     for kname, ds in sorted(per.items(), key=lambda kv: -sum(u for _, u in kv[1])):
         us = [u for _, u in ds]
-        out.append("| `%s` | %d | %.2f | %.2f | %.2f | %.2f |" % (_kname(kname).replace("|", "/")[:110], len(us),
+        out.append("| `%s` | %d | %.2f | %.2f | %.2f | %.2f |" % (_disp(kname), len(us),
                                                                  statistics.fmean(us), statistics.median(us),
                                                                  min(us), max(us)))
     out += ["", "Source: `%s` (rocprofv3 --kernel-trace --stats)." % os.path.relpath(path, trace_dir)]
     return "\n".join(out) + "\n"
 
 
-def pmc_summary(fetch_dir, write_dir, bench_log, commands):
+def _counter_per_kernel(d, counter):
+    """{kernel name: [(dispatch id, value)]} of one counter in a rocprofv3
+    --pmc output directory."""
+    rows, _ = _read_csv(os.path.join(d, "**", "*counter_collection.csv"))
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] == counter:
+            per.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return per
+
+
+# Kernels of the extras whose algorithmic bytes the bench line records:
+# (workload, kernel, (extras leg, key)). The chunk-width sweep launches the
+# split kernel at other widths too; those read the same K/V bytes.
+EXTRA_TRAFFIC = [
+    ("split-KV decode partials 16x32x131072x128 bf16", "fwd_kernel<Bf16, 128, 64, 4, false, 2>",
+     ("splitkv_decode", "algorithmic_bytes_split")),
+    ("causal GQA decode partials, 4 q vs 32768 cached, B=8, 32q/8kv", "fwd_kernel<Bf16, 128, 64, 4, true, 2>",
+     ("cache_gqa_decode", "algorithmic_bytes_split")),
+]
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
+SIMDS = 1024   # 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def sq_summary(sq_dir, bench_log, command):
+    """Markdown summary of one rocprofv3 --pmc pass over the SQ counters
+    (SQ_COUNTERS) of a bench run: the headline kernels' timed dispatches and
+    the MFMA busy share of every kernel of the run."""
+    line = _bench_line(bench_log)
+    ex = line["extras"]
+    per = {c: _counter_per_kernel(sq_dir, c) for c in SQ_COUNTERS}
+
+    def busy(mfma, grbm):   # GRBM_GUI_ACTIVE sums the XCDs' active cycles
+        return mfma / (grbm / XCDS * SIMDS)
+    md = ["# SQ counters: batched 4x16x4096x128 bf16 forward, and every kernel of the run", "",
+          "Command (MI355X, one GPU):", "", "    " + command, "",
+          "kernel_source_sha256: `%s`" % ex["kernel_source_sha256"], "",
+          "Medians over the timed dispatches (the bench line records how many launches came before them). MFMA busy "
+          "= SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs x %d SIMDs): the share of SIMD cycles the matrix "
+          "cores were busy at the clock the chip ran, not a share of the 2.4 GHz peak." % (XCDS, SIMDS), "",
+          "| counter | " + " | ".join(HEADLINE_KERNELS) + " |", "|---|" + "---|" * len(HEADLINE_KERNELS)]
+    med = {}
+    for tag, kname in HEADLINE_KERNELS.items():
+        skip = ex["launches_before_timing"][tag]
+        med[tag] = {}
+        for c in SQ_COUNTERS:
+            vals = [v for _, v in _dispatches(per[c], kname)[skip:skip + line["steps"]]]
+            if len(vals) != line["steps"]:
+                raise SystemExit("%s: %d timed dispatches of %s" % (c, len(vals), kname))
+            med[tag][c] = statistics.median(vals)
+    for c in SQ_COUNTERS:
+        md.append("| %s | " % c + " | ".join("%.4g" % med[tag][c] for tag in HEADLINE_KERNELS) + " |")
+    md.append("| MFMA busy | " + " | ".join("%.1f%%" % (100 * busy(med[t]["SQ_VALU_MFMA_BUSY_CYCLES"],
+                                                                  med[t]["GRBM_GUI_ACTIVE"])) for t in HEADLINE_KERNELS) + " |")
+    md += ["", "## MFMA busy of every kernel of the run (medians over all dispatches, warm-up included)", "",
+           "| kernel | dispatches | MFMA busy | SQ_INSTS_MFMA | SQ_LDS_BANK_CONFLICT |", "|---|---|---|---|---|"]
+    for kname in sorted(per["SQ_VALU_MFMA_BUSY_CYCLES"], key=lambda k_: -statistics.median(
+            [v for _, v in per["GRBM_GUI_ACTIVE"].get(k_, [(0, 0)])])):
+        m = statistics.median([v for _, v in per["SQ_VALU_MFMA_BUSY_CYCLES"][kname]])
+        g = statistics.median([v for _, v in per["GRBM_GUI_ACTIVE"].get(kname, [(0, 0)])])
+        if g <= 0:
+            continue
+        md.append("| `%s` | %d | %.1f%% | %.4g | %.4g |" % (
+            _disp(kname), len(per["SQ_VALU_MFMA_BUSY_CYCLES"][kname]), 100 * busy(m, g),
+            statistics.median([v for _, v in per["SQ_INSTS_MFMA"].get(kname, [(0, 0)])]),
+            statistics.median([v for _, v in per["SQ_LDS_BANK_CONFLICT"].get(kname, [(0, 0)])])))
+    return "\n".join(md) + "\n"
+
+
+def pmc_summary(fetch_dir, write_dir, bench_logs, commands):
     """HBM traffic of the headline kernels from FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled by what the same counter reads for the
     bench's plain 256 MiB device copy; medians over the timed dispatches.
-    Writes the committed summary (.md and .json)."""
-    line = _bench_line(bench_log)
+    Each counter comes from a bench run of its own, whose log (in the order
+    FETCH_SIZE, WRITE_SIZE) says which dispatches were timed. Writes the
+    committed summary (.md and .json)."""
+    if len(bench_logs) != 2:
+        raise SystemExit("--pmc-summary needs two --bench-log files: the FETCH_SIZE run's, then the WRITE_SIZE run's")
+    lines = [_bench_line(b) for b in bench_logs]
+    if lines[0]["extras"]["kernel_source_sha256"] != lines[1]["extras"]["kernel_source_sha256"]:
+        raise SystemExit("the two counter runs were taken on different kernel sources")
+    line = lines[0]
     ex = line["extras"]
-    res = {}
-    for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        rows, _ = _read_csv(os.path.join(d, "**", "*counter_collection.csv"))
-        per = {}
-        for r in rows:
-            if r["Counter_Name"] == counter:
-                per.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    res, pers = {}, {}
+    for name, d, counter, run in (("fetch", fetch_dir, "FETCH_SIZE", lines[0]), ("write", write_dir, "WRITE_SIZE",
+                                                                                 lines[1])):
+        per = pers[name] = _counter_per_kernel(d, counter)
         copies = [v for k_, vs in per.items() if "copyBuffer" in k_ for _, v in vs]
         if not copies:
             raise SystemExit("no device copy kernel in the %s run" % counter)
@@ -1180,9 +1267,9 @@ def pmc_summary(fetch_dir, write_dir, bench_log, commands):
         res[name] = {"calibration_kib": cal_kib, "scale": scale}
         for tag, kname in HEADLINE_KERNELS.items():
             ds = _dispatches(per, kname)
-            skip = ex["launches_before_timing"][tag]
-            vals = [v for _, v in ds[skip:skip + line["steps"]]]
-            if len(vals) != line["steps"]:
+            skip = run["extras"]["launches_before_timing"][tag]
+            vals = [v for _, v in ds[skip:skip + run["steps"]]]
+            if len(vals) != run["steps"]:
                 raise SystemExit("%s run: %d timed dispatches of %s" % (counter, len(vals), kname))
             res[name][tag] = statistics.median(vals) * scale * 1024
     algo = line["config"]["algorithmic_bytes_per_launch"]
@@ -1206,6 +1293,26 @@ def pmc_summary(fetch_dir, write_dir, bench_log, commands):
         p = js["per_launch"][tag]
         md.append("| %s | %.1f | %.1f | %.1f | %.2f |" % (tag, p["fetch_bytes"] / 1e6, p["write_bytes"] / 1e6,
                                                          algo / 1e6, p["ratio"]))
+    # Every kernel of the runs (the extras too, when the runs had them):
+    # medians over all dispatches, warm-up included.
+    known = {}
+    for what, kname, (leg, key) in EXTRA_TRAFFIC:
+        if leg in lines[0]["extras"] and leg in lines[1]["extras"]:
+            known[_kname(kname)] = (what, lines[0]["extras"][leg][key])
+    md += ["", "## Every kernel of the runs (medians over all dispatches, warm-up included)", "",
+           "| kernel | dispatches | fetch MB | write MB | algorithmic MB | ratio |", "|---|---|---|---|---|---|"]
+    js["per_kernel"] = {}
+    for kname in sorted(set(pers["fetch"]) & set(pers["write"]),
+                        key=lambda k_: -statistics.median([v for _, v in pers["fetch"][k_]])):
+        fb = statistics.median([v for _, v in pers["fetch"][kname]]) * res["fetch"]["scale"] * 1024
+        wb = statistics.median([v for _, v in pers["write"][kname]]) * res["write"]["scale"] * 1024
+        kn = _kname(kname)
+        what, ab = known.get(kn, (None, None))
+        js["per_kernel"][kn] = {"dispatches": len(pers["fetch"][kname]), "fetch_bytes": fb, "write_bytes": wb,
+                                "algorithmic_bytes": ab, "workload": what}
+        md.append("| `%s`%s | %d | %.1f | %.1f | %s | %s |" % (
+            _disp(kname), (" (%s)" % what) if what else "", len(pers["fetch"][kname]), fb / 1e6,
+            wb / 1e6, "%.1f" % (ab / 1e6) if ab else "", "%.2f" % ((fb + wb) / ab) if ab else ""))
     base = os.path.splitext(PMC_SUMMARY)[0]
     with open(base + ".json", "w") as fh:
         json.dump(js, fh, indent=1)
@@ -1227,11 +1334,15 @@ def main():
     ap.add_argument("--variants", action="store_true")
     ap.add_argument("--trace-summary", metavar="DIR")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--bench-log")
+    ap.add_argument("--sq-summary", metavar="DIR")
+    ap.add_argument("--bench-log", action="append", default=[])
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
     if args.trace_summary:
-        sys.stdout.write(trace_summary(args.trace_summary, args.bench_log, " ".join(args.command)))
+        sys.stdout.write(trace_summary(args.trace_summary, args.bench_log[0], " ".join(args.command)))
+        return
+    if args.sq_summary:
+        sys.stdout.write(sq_summary(args.sq_summary, args.bench_log[0], " ".join(args.command)))
         return
     if args.pmc_summary:
         print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.bench_log, args.command)))

@@ -854,21 +854,29 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(const FwdParams p) {
   }
 }
 
-// Merge of split-KV partial states: one wave per row, partials summed in
-// ascending chunk order ("Attention algorithms and data movement", lesson 01).
+// Merge of split-KV partial states, one row per single-wave workgroup (a
+// few hundred rows then still spread over every CU); the partials are summed
+// in ascending chunk order ("Attention algorithms and data movement", lesson
+// 01). The row max and the chunk weights exp(m_c - M) are taken for 64
+// chunks at a time, one chunk per lane; the ordered sums then read the
+// weights back lane by lane while the accumulator rows of 16 chunks are
+// loaded together.
 template <class E, int D>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
-                                                    const float* __restrict__ pacc, int64_t rows, int nchunks,
-                                                    uint16_t* __restrict__ o, float* __restrict__ lse) {
+__global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
+                                                   const float* __restrict__ pacc, int64_t rows, int nchunks,
+                                                   uint16_t* __restrict__ o, float* __restrict__ lse) {
   constexpr int PER = D >= 64 ? D / 64 : 1;  // d values per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int BATCH = 16;                  // chunks whose accumulator rows are in flight together
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
   if (row >= rows) return;
   const bool lane_ok = lane * PER < D;
   const float* rm = pm + row * nchunks;
   const float* rl = pl + row * nchunks;
   float big_m = -INFINITY;
-  for (int ch = 0; ch < nchunks; ++ch) big_m = fmaxf(big_m, rm[ch]);
+  for (int ch = lane; ch < nchunks; ch += 64) big_m = fmaxf(big_m, rm[ch]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) big_m = fmaxf(big_m, __shfl_xor(big_m, off));
   uint16_t* orow = o + row * D;
   if (big_m == -INFINITY) {  // every partial empty: O = 0, lse = -inf
     if (lane_ok)
@@ -879,13 +887,29 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm
   float big_l = 0.f;
   float a[PER];
   for (int e = 0; e < PER; ++e) a[e] = 0.f;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const float mc = rm[ch];
-    const float wgt = (mc == -INFINITY) ? 0.f : expf(mc - big_m);
-    big_l += wgt * rl[ch];
-    if (lane_ok) {
-      const float* src = pacc + (row * nchunks + ch) * D + lane * PER;
-      for (int e = 0; e < PER; ++e) a[e] += wgt * src[e];
+  const float* src = pacc + row * nchunks * D + (lane_ok ? lane * PER : 0);
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int n = min(64, nchunks - c0);
+    float wgt = 0.f, lc = 0.f;   // this lane's chunk c0 + lane: weight and partial sum
+    if (lane < n) {
+      const float mc = rm[c0 + lane];
+      wgt = (mc == -INFINITY) ? 0.f : expf(mc - big_m);
+      lc = rl[c0 + lane];
+    }
+    for (int j0 = 0; j0 < n; j0 += BATCH) {
+      float v[BATCH][PER];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[j][e] = (lane_ok && j0 + j < n) ? src[(int64_t)(c0 + j0 + j) * D + e] : 0.f;
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        if (j0 + j >= n) break;
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j0 + j));
+        big_l = fmaf(wj, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lc), j0 + j)), big_l);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) a[e] = fmaf(wj, v[j][e], a[e]);
+      }
     }
   }
   const float inv = 1.f / big_l;

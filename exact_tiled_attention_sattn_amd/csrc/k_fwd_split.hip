@@ -12,8 +12,7 @@ void go(const FwdParams& p, int64_t grid, hipStream_t s) {
 template <class E, int D>
 void go_merge(const float* pm, const float* pl, const float* pacc, int64_t rows, int nchunks, uint16_t* o, float* lse,
               hipStream_t s) {
-  const int64_t grid = (rows + 3) / 4;
-  hipLaunchKernelGGL((merge_kernel<E, D>), dim3((unsigned)grid), dim3(256), 0, s, pm, pl, pacc, rows, nchunks, o, lse);
+  hipLaunchKernelGGL((merge_kernel<E, D>), dim3((unsigned)rows), dim3(64), 0, s, pm, pl, pacc, rows, nchunks, o, lse);
 }
 }  // namespace
 

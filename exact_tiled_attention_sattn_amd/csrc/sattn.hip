@@ -645,8 +645,7 @@ int sattn_merge(int dtype, const float* part_m, const float* part_l, const float
                   range_of(part_acc, abytes, "part_acc")};
   Range outs[2] = {range_of(o, obytes, "o"), range_of(lse, rows * 4, "lse")};
   if ((st = check_alias(ins, 3, outs, 2))) return st;
-  const int64_t grid = (rows + 3) / 4;
-  if (grid >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
+  if (rows >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");  // one workgroup per row
   launch_merge(dtype, (int)D, part_m, part_l, part_acc, rows, (int)C, (uint16_t*)o, lse, (hipStream_t)stream);
   return launch_status();
 }

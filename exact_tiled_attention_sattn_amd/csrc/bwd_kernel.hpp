@@ -11,9 +11,13 @@
 // Two kernels, no atomics, every sum in a fixed order:
 //   bwd_dq_kernel   -- a wave owns 32 queries and walks 64-key K/V tiles
 //                      (the forward's walk); it also forms Delta and stores it.
-//   bwd_dkdv_kernel -- a wave owns 32 keys and walks 64-query Q/dO tiles of
-//                      every query head of its KV head; it runs after the
-//                      dQ kernel on the same stream and reads Delta.
+//   bwd_dkdv_roles_kernel (D = 128) -- two waves of one SIMD own 32 keys
+//                      and walk 64-query Q/dO tiles of every query head of
+//                      their KV head, one forming P and dV, the other dP, dS
+//                      and dK; it runs after the dQ kernel on the same stream
+//                      and reads Delta.
+//   bwd_dkdv_kernel (D = 32, 64) -- the same walk, one wave per 32 keys
+//                      forming both.
 // MFMA operand layouts follow the forward: a lane owns one row of the 32x32
 // accumulator's columns; operands of the transposed products come from
 // ds_read_b64_tr_b16 on the natural [row][d] LDS layout, in the row order
@@ -326,6 +330,134 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdParams p) {
                         p.dq + qbase + (int64_t)wave_u * 32 * q_rs, q_rs, nq - wave_u * 32);
 }
 
+// Work of one dK/dV workgroup: up to 128 keys of one KV head, and the walk
+// over the 64-query tiles of every query head of the group that see them.
+// Workgroup -> (KV head, key tile): KV heads contiguous per XCD (varlen: KV
+// head, then sequence), the keys that see the most queries (causal: the
+// earliest) first.
+template <int D, bool CAUSAL, int LAYOUT>
+struct KvWalk {
+  static constexpr bool VARLEN = LAYOUT == BWD_VARLEN;
+  static constexpr bool SPARSE = LAYOUT == BWD_SPARSE;
+  static constexpr int BNK = 128, BMQ = 64;
+  static constexpr int TILE = BMQ * D;   // elements of one Q or dO tile
+  int grp;
+  int len, qlen, off, k0, g;   // keys and queries of the slice, position of query 0, first key, KV head
+  int tok0, bq;                // varlen: first token of the sequence; batched: batch index
+  int64_t kvbase, q_rs, kv_rs; // key k0 of k/v/dk/dv in elements; row strides
+  int nkeys;                   // keys of this workgroup
+  int t_begin, per_head, npre, band0, nsteps;
+
+  // false if the workgroup has no keys (uniform over the workgroup)
+  __device__ __forceinline__ bool init(const BwdParams& p) {
+    grp = p.hq / p.hkv;
+    off = 0;
+    tok0 = 0;
+    bq = 0;
+    const int lin = xcd_linear(blockIdx.x);
+    if constexpr (VARLEN) {
+      const int per_g = p.nseq * p.nkt;
+      g = lin / per_g;
+      const int sq = (lin % per_g) / p.nkt;
+      const int kt = lin % p.nkt;
+      int a = p.cu_seqlens[sq], e = p.cu_seqlens[sq + 1];
+      a = min(max(a, 0), p.total);
+      e = min(max(e, a), p.total);
+      len = e - a;
+      qlen = len;
+      tok0 = a;
+      k0 = kt * BNK;
+      if (k0 >= len) return false;
+      q_rs = (int64_t)p.hq * D;
+      kv_rs = (int64_t)p.hkv * D;
+      kvbase = (int64_t)(a + k0) * kv_rs + (int64_t)g * D;
+    } else {
+      const int kvs = lin / p.nkt;   // b * Hkv + g
+      const int kt = lin % p.nkt;
+      bq = kvs / p.hkv;
+      g = kvs % p.hkv;
+      len = p.nk;
+      qlen = p.n;
+      off = p.off;
+      k0 = kt * BNK;
+      q_rs = D;
+      kv_rs = D;
+      kvbase = ((int64_t)kvs * p.nk + k0) * D;
+    }
+    nkeys = min(BNK, len - k0);
+    // query tiles: every query head of the group, causal from the tile
+    // holding k0; under the sparse operator (no global key among the keys)
+    // only the tiles of global queries [t_begin, t_begin + npre) and then the
+    // window band from band0
+    t_begin = CAUSAL ? max(0, k0 - off) / BMQ : 0;
+    const int nqt = (qlen + BMQ - 1) / BMQ;
+    per_head = nqt - t_begin;
+    npre = 0;
+    band0 = t_begin;
+    if constexpr (SPARSE) {
+      if (k0 >= p.n_global) {
+        const int pre_hi = max(t_begin, min(nqt, (p.n_global + BMQ - 1) / BMQ));
+        npre = pre_hi - t_begin;
+        const int lo = p.win_right < 0 ? 0 : max(0, k0 - p.win_right) / BMQ;
+        const int hi = p.win_left < 0 ? nqt : min(nqt, (k0 + BNK - 1 + p.win_left) / BMQ + 1);
+        band0 = max(pre_hi, lo);
+        per_head = npre + max(0, hi - band0);
+      }
+    }
+    nsteps = per_head * grp;
+    return true;
+  }
+  // the query tiles of query head hh start at qhead(hh) in q/dout and at
+  // lhead(hh) in lse/Delta
+  __device__ __forceinline__ int64_t qhead(const BwdParams& p, int hh) const {
+    return VARLEN ? (int64_t)tok0 * q_rs + (int64_t)hh * D : ((int64_t)bq * p.hq + hh) * p.n * D;
+  }
+  __device__ __forceinline__ int64_t lhead(const BwdParams& p, int hh) const {
+    return VARLEN ? (int64_t)hh * p.total + tok0 : ((int64_t)bq * p.hq + hh) * p.n;
+  }
+  // step it: its query head, and its first query
+  __device__ __forceinline__ int head(int it) const { return g * grp + it / per_head; }
+  __device__ __forceinline__ int q0(int it) const {
+    const int i = it % per_head;
+    return (i < npre ? t_begin + i : band0 + (i - npre)) * BMQ;
+  }
+  __device__ __forceinline__ uint32_t row_bytes() const { return (uint32_t)q_rs * 2u; }
+  // loads of step it's Q and dO tiles, lse and Delta (wave 0) into sb
+  template <int NW>
+  __device__ __forceinline__ void issue(const BwdParams& p, const TileLoader<D, NW>& ld, int it, uint16_t* sb,
+                                        int wave_u, int lane) const {
+    const int hh = head(it);
+    const int q0_ = q0(it);
+    const int rows = min(BMQ, qlen - q0_);
+    const uint32_t rb = row_bytes();
+    const int64_t qoff = qhead(p, hh) + (int64_t)q0_ * q_rs;
+    const int64_t loff = lhead(p, hh) + q0_;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.q + qoff), (short)0, (int)(rows * rb), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.dout + qoff), (short)0, (int)(rows * rb), 0x00020000);
+#pragma unroll
+    for (int r = 0; r < BMQ / 64; ++r) {
+      ld.issue(rq, (uint32_t)(r * 64) * rb, sb + r * 64 * D, wave_u);
+      ld.issue(rd, (uint32_t)(r * 64) * rb, sb + TILE + r * 64 * D, wave_u);
+    }
+    if (wave_u == 0) {   // lse and Delta of the tile's rows, 4 bytes per lane
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.lse + loff), (short)0, rows * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.delta + loff), (short)0, rows * 4, 0x00020000);
+#pragma unroll
+      for (int r = 0; r < BMQ / 64; ++r) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + r * 128),
+                                                 4, (uint32_t)lane * 4u, (uint32_t)r * 256u, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            re, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + 2 * BMQ + r * 128), 4, (uint32_t)lane * 4u,
+            (uint32_t)r * 256u, 0, 0);
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------- dK, dV
 template <class E, int D, bool CAUSAL, int LAYOUT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
@@ -339,53 +471,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[BUF];
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[BUF];
 
-  // block -> (KV head, key tile); KV heads contiguous per XCD (varlen: KV
-  // head, then sequence), the keys that see the most queries (causal: the
-  // earliest) first. kvbase is key k0 of k/v/dk/dv in elements; the query
-  // tiles of query head hh start at qhead(hh) in q/dout and at lhead(hh) in
-  // lse/Delta.
-  const int grp = p.hq / p.hkv;
-  // len: keys of the slice; qlen: its queries; off: position of query 0
-  int len, qlen, off = 0, k0, g, tok0 = 0, bq = 0;
-  int64_t kvbase, q_rs, kv_rs;
-  if constexpr (VARLEN) {
-    const int lin = xcd_linear(blockIdx.x);
-    const int per_g = p.nseq * p.nkt;
-    g = lin / per_g;
-    const int sq = (lin % per_g) / p.nkt;
-    const int kt = lin % p.nkt;
-    int a = p.cu_seqlens[sq], e = p.cu_seqlens[sq + 1];
-    a = min(max(a, 0), p.total);
-    e = min(max(e, a), p.total);
-    len = e - a;
-    qlen = len;
-    tok0 = a;
-    k0 = kt * BNK;
-    if (k0 >= len) return;  // uniform over the workgroup
-    q_rs = (int64_t)p.hq * D;
-    kv_rs = (int64_t)p.hkv * D;
-    kvbase = (int64_t)(a + k0) * kv_rs + (int64_t)g * D;
-  } else {
-    const int lin = xcd_linear(blockIdx.x);
-    const int kvs = lin / p.nkt;                  // b * Hkv + g
-    const int kt = lin % p.nkt;
-    bq = kvs / p.hkv;
-    g = kvs % p.hkv;
-    len = p.nk;
-    qlen = p.n;
-    off = p.off;
-    k0 = kt * BNK;
-    q_rs = D;
-    kv_rs = D;
-    kvbase = ((int64_t)kvs * p.nk + k0) * D;
-  }
-  auto qhead = [&](int hh) -> int64_t {
-    return VARLEN ? (int64_t)tok0 * q_rs + (int64_t)hh * D : ((int64_t)bq * p.hq + hh) * p.n * D;
-  };
-  auto lhead = [&](int hh) -> int64_t {
-    return VARLEN ? (int64_t)hh * p.total + tok0 : ((int64_t)bq * p.hq + hh) * p.n;
-  };
-  const int nkeys = min(BNK, len - k0);
+  KvWalk<D, CAUSAL, LAYOUT> wk;
+  if (!wk.init(p)) return;   // uniform over the workgroup
+  const int grp = wk.grp, len = wk.len, qlen = wk.qlen, off = wk.off, k0 = wk.k0, g = wk.g;
+  const int64_t kvbase = wk.kvbase, kv_rs = wk.kv_rs;
+  const int nkeys = wk.nkeys;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -415,59 +505,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
       adv[db][r] = 0.f;
     }
 
-  // query tiles: every query head of the group, causal from the tile holding
-  // k0; under the sparse operator (no global key among the keys) only the
-  // tiles of global queries [t_begin, t_begin + npre) and then the window
-  // band from band0
-  const int t_begin = CAUSAL ? max(0, k0 - off) / BMQ : 0;
-  const int nqt = (qlen + BMQ - 1) / BMQ;
-  int per_head = nqt - t_begin, npre = 0, band0 = t_begin;
-  if constexpr (SPARSE) {
-    if (k0 >= p.n_global) {
-      const int pre_hi = max(t_begin, min(nqt, (p.n_global + BMQ - 1) / BMQ));
-      npre = pre_hi - t_begin;
-      const int lo = p.win_right < 0 ? 0 : max(0, k0 - p.win_right) / BMQ;
-      const int hi = p.win_left < 0 ? nqt : min(nqt, (k0 + BNK - 1 + p.win_left) / BMQ + 1);
-      band0 = max(pre_hi, lo);
-      per_head = npre + max(0, hi - band0);
-    }
-  }
-  auto qtile_of = [&](int i) { return i < npre ? t_begin + i : band0 + (i - npre); };
-  const int nsteps = per_head * grp;
-  const uint32_t row_bytes = (uint32_t)q_rs * 2u;
+  const int nsteps = wk.nsteps;
   TileLoader<D, NW> ld;
-  ld.init(wave, lane, row_bytes);
-  auto issue_step = [&](int it, uint16_t* sb) {
-    const int hh = g * grp + it / per_head;
-    const int t = qtile_of(it % per_head);
-    const int q0 = t * BMQ;
-    const int rows = min(BMQ, qlen - q0);
-    const int64_t qoff = qhead(hh) + (int64_t)q0 * q_rs;
-    const int64_t loff = lhead(hh) + q0;
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.q + qoff), (short)0, (int)(rows * row_bytes), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.dout + qoff), (short)0, (int)(rows * row_bytes), 0x00020000);
-#pragma unroll
-    for (int r = 0; r < BMQ / 64; ++r) {
-      ld.issue(rq, (uint32_t)(r * 64) * row_bytes, sb + r * 64 * D, wave_u);
-      ld.issue(rd, (uint32_t)(r * 64) * row_bytes, sb + TILE + r * 64 * D, wave_u);
-    }
-    if (wave_u == 0) {   // lse and Delta of the tile's rows, 4 bytes per lane
-      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.lse + loff), (short)0, rows * 4, 0x00020000);
-      const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.delta + loff), (short)0, rows * 4, 0x00020000);
-#pragma unroll
-      for (int r = 0; r < BMQ / 64; ++r) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + r * 128),
-                                                 4, (uint32_t)lane * 4u, (uint32_t)r * 256u, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            re, (__attribute__((address_space(3))) void*)(sb + 2 * TILE + 2 * BMQ + r * 128), 4, (uint32_t)lane * 4u,
-            (uint32_t)r * 256u, 0, 0);
-      }
-    }
-  };
+  ld.init(wave, lane, wk.row_bytes());
+  auto issue_step = [&](int it, uint16_t* sb) { wk.issue(p, ld, it, sb, wave_u, lane); };
 
   int aofs[KK];
 #pragma unroll
@@ -555,8 +596,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (it + 1 < nsteps) issue_step(it + 1, nxt);
-    const int q0 = qtile_of(it % per_head) * BMQ;
-    const int hh = g * grp + it / per_head;
+    const int q0 = wk.q0(it);
+    const int hh = wk.head(it);
     if (!wave_active) return;
     // sparse: need / no mask needed for 32-query block qb0 against the wave's
     // keys (one mask row block, one key block)
@@ -638,6 +679,249 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
                         nkeys - wave_u * 32);
   store_tile_rows<E, D>(adv, 1.0f, sbuf1 + wave_u * 32 * D, p.dv + kvbase + (int64_t)wave_u * 32 * kv_rs, kv_rs,
                         nkeys - wave_u * 32);
+}
+
+
+// ---------------------------------------------------------------- dK, dV in two roles (D = 128)
+// 8 waves and 128 keys per workgroup; waves w and w + 4, the two waves of one
+// SIMD, own the same 32 keys. Wave w (the P role) forms S = Q K^T, the
+// probabilities P and dV^T += dO^T P; wave w + 4 (the dS role) forms
+// dP = dO V^T, dS = P (dP - Delta) with P taken from its partner through
+// LDS, and dK^T += Q^T dS. A 64-query step has two phases split by a
+// barrier: S and P beside dP, then dV beside dS and dK, so each wave of a
+// SIMD issues 16 MFMAs per 32-query block in each phase and one wave's
+// exponentials and dS arithmetic run beside the other's MFMAs. P goes through
+// LDS in fp32, so every value and every accumulation order is the one-wave
+// kernel's (bwd_dkdv_kernel), bit for bit.
+template <class E, int D, bool CAUSAL, int LAYOUT>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_roles_kernel(const BwdParams p) {
+  constexpr bool VARLEN = LAYOUT == BWD_VARLEN;
+  constexpr bool SPARSE = LAYOUT == BWD_SPARSE;
+  constexpr int NW = 8, BNK = 128, BMQ = 64;
+  constexpr int KK = D / 16, DB = D / 32;
+  constexpr int TILE = BMQ * D;                 // elements of one Q or dO tile
+  constexpr int BUF = 2 * TILE + 2 * BMQ * 2;   // Q, dO, then lse and Delta (fp32)
+  static_assert(D == 128, "two-role layout: 8 waves of 32 keys, D = 128");
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[BUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[BUF];
+  // P of the current step: [key block][32-query block][register group][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 pex[4][2][4][64];
+
+  KvWalk<D, CAUSAL, LAYOUT> wk;
+  if (!wk.init(p)) return;   // uniform over the workgroup
+  const int grp = wk.grp, len = wk.len, qlen = wk.qlen, off = wk.off, k0 = wk.k0, g = wk.g;
+  const int64_t kvbase = wk.kvbase, kv_rs = wk.kv_rs;
+  const int nkeys = wk.nkeys;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const bool role_p = wave_u < 4;
+  const int kw = wave_u & 3;                    // the pair's 32-key block
+  const int krow = kw * 32 + l32;
+  const bool key_ok = krow < nkeys;
+  const int my_key = k0 + krow;
+  const bool wave_active = kw * 32 < nkeys;
+  const int wave_first_key = k0 + kw * 32;
+
+  const int nsteps = wk.nsteps;
+  TileLoader<D, NW> ld;
+  ld.init(wave, lane, wk.row_bytes());
+  auto issue_step = [&](int it, uint16_t* sb) { wk.issue(p, ld, it, sb, wave_u, lane); };
+
+  int aofs[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) aofs[kk] = l32 * D + (((kk * 2 + hf) ^ swz<D>(l32)) * 8);
+  const int g16 = lane >> 4;
+  const int tr_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+  int tofs[2][DB];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = db * 32 + 16 * (g16 & 1) + 4 * (lane & 3);
+      const int row = tr_row + 8 * x;
+      tofs[x][db] = row * D + (((d0 >> 3) ^ swz<D>(row)) * 8) + (d0 & 7);
+    }
+
+
+  // Which 32-query blocks of a step a pair computes, and which need the
+  // element mask (queries past the end; causal: a query before a key of the
+  // pair; sparse: a pair the rule drops). Both roles take the same decisions.
+  const int wkey1 = min(wave_first_key + 31, len - 1);
+  auto blk_need = [&](int hh, int qb0) {
+    if (CAUSAL && qb0 + off + 31 < wave_first_key) return false;   // every query precedes the keys
+    if constexpr (SPARSE)
+      return qb0 < qlen && sparse_bit(p, hh, qb0, wave_first_key) &&
+             sparse_any(p, qb0, min(qb0 + 31, qlen - 1), wave_first_key, wkey1);
+    return true;
+  };
+  auto blk_edge = [&](int qb0) {
+    return qb0 + 32 > qlen || (CAUSAL && qb0 + off < wave_first_key + 31) ||
+           (SPARSE && !sparse_all(p, qb0, min(qb0 + 31, qlen - 1), wave_first_key, wkey1));
+  };
+  // A operand of S = Q K^T / dP = dO V^T: 32 rows of the tile, k-steps of 16 d
+  auto rows_mfma = [&](const uint16_t* sT, int qb, const u32x4 (&breg)[KK], f32x16& acc) {
+    u32x4 a[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) a[kk] = *(const u32x4*)(sT + aofs[kk] + qb * 32 * D);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) acc = E::mfma32(a[kk], breg[kk], acc);
+  };
+  // acc^T += T^T X for one 32-query block: T^T from transposing reads of the
+  // tile, X the packed block (16 queries per MFMA)
+  auto tr_mfma = [&](const uint16_t* sT, int qb, const u32x4 (&x)[2], f32x16 (&acc)[DB]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int qrow = (qb * 32 + half * 16) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 a0 = lds_read_tr16(sT + tofs[0][db] + qrow);
+        const u32x2 a1 = lds_read_tr16(sT + tofs[1][db] + qrow);
+        acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, x[half], acc[db]);
+      }
+    }
+  };
+  auto pack16 = [&](const f32x16& v, u32x4 (&x)[2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int o8 = half * 8;
+      x[half] = u32x4{E::pack2(v[o8 + 0], v[o8 + 1]), E::pack2(v[o8 + 2], v[o8 + 3]),
+                      E::pack2(v[o8 + 4], v[o8 + 5]), E::pack2(v[o8 + 6], v[o8 + 7])};
+    }
+  };
+
+  f32x16 acc[DB];   // dV (P role) or dK (dS role), transposed: [d][key]
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  if (nsteps > 0) issue_step(0, sbuf0);
+
+  if (role_p) {
+    // ---- P role: K as the B operand of S = Q K^T
+    u32x4 kreg[KK];
+    {
+      const int64_t o_ = kvbase + (int64_t)krow * kv_rs + hf * 8;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kreg[kk] = key_ok ? *(const u32x4*)(p.k + o_ + kk * 16) : u32x4{0, 0, 0, 0};
+    }
+    auto step = [&](int it, const uint16_t* cur, uint16_t* nxt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();   // tile it visible; every wave is done with tile it-1 and the previous P
+      if (it + 1 < nsteps) issue_step(it + 1, nxt);
+      const int q0 = wk.q0(it);
+      const int hh = wk.head(it);
+      const uint16_t* sQ = cur;
+      const uint16_t* sD = cur + TILE;
+      const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
+      u32x4 pb[2][2];
+      // P = exp2(S c - lse log2 e) of block qb in place, masked on edge
+      // blocks, and to LDS for the partner
+      auto probs = [&](int qb, int qb0, f32x16& s, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 l4 = *(const f32x4*)(sL + qb * 32 + 8 * g4 + 4 * hf);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = g4 * 4 + i;
+            float x = fast_exp2(fmaf(s[r], p.c, -l4[i] * kLog2e));
+            if constexpr (EDGE) {
+              const int qi = qb0 + 8 * g4 + 4 * hf + i;
+              if (qi >= qlen || (CAUSAL && my_key > qi + off) || (SPARSE && !sparse_pair(p, qi, my_key))) x = 0.f;
+            }
+            s[r] = x;
+          }
+          pex[kw][qb][g4][lane] = f32x4{s[g4 * 4 + 0], s[g4 * 4 + 1], s[g4 * 4 + 2], s[g4 * 4 + 3]};
+        }
+      };
+      if (wave_active) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int qb0 = q0 + qb * 32;
+          if (!blk_need(hh, qb0)) continue;
+          f32x16 s;
+          rows_mfma(sQ, qb, kreg, s);
+          if (blk_edge(qb0)) probs(qb, qb0, s, std::true_type{});
+          else probs(qb, qb0, s, std::false_type{});
+          pack16(s, pb[qb]);
+        }
+      }
+      __syncthreads();   // P of both blocks in LDS
+      if (wave_active) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          if (blk_need(hh, q0 + qb * 32)) tr_mfma(sD, qb, pb[qb], acc);   // dV^T += dO^T P
+      }
+    };
+    int it = 0;
+    for (; it + 1 < nsteps; it += 2) {
+      step(it, sbuf0, sbuf1);
+      step(it + 1, sbuf1, sbuf0);
+    }
+    if (it < nsteps) step(it, sbuf0, sbuf1);
+    __syncthreads();   // every wave is done with the tile buffers, which stage the stores
+    store_tile_rows<E, D>(acc, 1.0f, sbuf0 + kw * 32 * D, p.dv + kvbase + (int64_t)kw * 32 * kv_rs, kv_rs,
+                          nkeys - kw * 32);
+  } else {
+    // ---- dS role: V as the B operand of dP = dO V^T
+    u32x4 vreg[KK];
+    {
+      const int64_t o_ = kvbase + (int64_t)krow * kv_rs + hf * 8;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) vreg[kk] = key_ok ? *(const u32x4*)(p.v + o_ + kk * 16) : u32x4{0, 0, 0, 0};
+    }
+    auto step = [&](int it, const uint16_t* cur, uint16_t* nxt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (it + 1 < nsteps) issue_step(it + 1, nxt);
+      const int q0 = wk.q0(it);
+      const int hh = wk.head(it);
+      const uint16_t* sQ = cur;
+      const uint16_t* sD = cur + TILE;
+      const float* sE = reinterpret_cast<const float*>(cur + 2 * TILE) + BMQ;
+      f32x16 dp[2];
+      if (wave_active) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          if (blk_need(hh, q0 + qb * 32)) rows_mfma(sD, qb, vreg, dp[qb]);
+      }
+      __syncthreads();   // the partner's P of both blocks in LDS
+      // dS = P (dP - Delta) of block qb, packed
+      auto dscores = [&](int qb, u32x4 (&sb)[2]) {
+        f32x16 ds;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 pr = pex[kw][qb][g4][lane];
+          const f32x4 d4 = *(const f32x4*)(sE + qb * 32 + 8 * g4 + 4 * hf);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ds[g4 * 4 + i] = pr[i] * (dp[qb][g4 * 4 + i] - d4[i]);
+        }
+        pack16(ds, sb);
+      };
+      if (wave_active) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (!blk_need(hh, q0 + qb * 32)) continue;
+          u32x4 sb[2];
+          dscores(qb, sb);
+          tr_mfma(sQ, qb, sb, acc);   // dK^T += Q^T dS
+        }
+      }
+    };
+    int it = 0;
+    for (; it + 1 < nsteps; it += 2) {
+      step(it, sbuf0, sbuf1);
+      step(it + 1, sbuf1, sbuf0);
+    }
+    if (it < nsteps) step(it, sbuf0, sbuf1);
+    __syncthreads();
+    store_tile_rows<E, D>(acc, p.scale, sbuf1 + kw * 32 * D, p.dk + kvbase + (int64_t)kw * 32 * kv_rs, kv_rs,
+                          nkeys - kw * 32);
+  }
 }
 
 }  // namespace sattn

@@ -10,26 +10,35 @@ void go(bool causal, const BwdParams& p, int64_t grid_q, int64_t grid_kv, hipStr
     constexpr int NWQ = bwd_dq_waves(D, true, BWD_SPARSE);
     hipLaunchKernelGGL((bwd_dq_kernel<E, D, true, BWD_SPARSE, NWQ>), dim3((unsigned)grid_q), dim3(NWQ * 64), 0, s, p);
     if (grid_kv > 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, true, BWD_SPARSE>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+      launch_dkdv<E, D, true, BWD_SPARSE>(p, grid_kv, s);
   } else {
     constexpr int NWQ = bwd_dq_waves(D, false, BWD_SPARSE);
     hipLaunchKernelGGL((bwd_dq_kernel<E, D, false, BWD_SPARSE, NWQ>), dim3((unsigned)grid_q), dim3(NWQ * 64), 0, s, p);
     if (grid_kv > 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, false, BWD_SPARSE>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+      launch_dkdv<E, D, false, BWD_SPARSE>(p, grid_kv, s);
   }
 }
 }  // namespace
 
 // Explicit instantiations, so that every kernel of this layout has its
-// device code and host stub in this object.
+// device code and host stub in this object: dQ for every D; dK/dV in two
+// roles at D = 128, one wave per key block below.
 #define SATTN_INST(E_, D_)                                                                      \
   template __global__ void bwd_dq_kernel<E_, D_, true, BWD_SPARSE, bwd_dq_waves(D_, true, BWD_SPARSE)>(const BwdParams);  \
-  template __global__ void bwd_dq_kernel<E_, D_, false, BWD_SPARSE, bwd_dq_waves(D_, false, BWD_SPARSE)>(const BwdParams); \
-  template __global__ void bwd_dkdv_kernel<E_, D_, true, BWD_SPARSE>(const BwdParams);                                  \
+  template __global__ void bwd_dq_kernel<E_, D_, false, BWD_SPARSE, bwd_dq_waves(D_, false, BWD_SPARSE)>(const BwdParams);
+#define SATTN_INST_KV(E_, D_)                                                         \
+  template __global__ void bwd_dkdv_kernel<E_, D_, true, BWD_SPARSE>(const BwdParams);  \
   template __global__ void bwd_dkdv_kernel<E_, D_, false, BWD_SPARSE>(const BwdParams);
+#define SATTN_INST_KV2(E_)                                                                 \
+  template __global__ void bwd_dkdv_roles_kernel<E_, 128, true, BWD_SPARSE>(const BwdParams);  \
+  template __global__ void bwd_dkdv_roles_kernel<E_, 128, false, BWD_SPARSE>(const BwdParams);
 SATTN_INST(Bf16, 32) SATTN_INST(Bf16, 64) SATTN_INST(Bf16, 128)
 SATTN_INST(F16, 32) SATTN_INST(F16, 64) SATTN_INST(F16, 128)
+SATTN_INST_KV(Bf16, 32) SATTN_INST_KV(Bf16, 64) SATTN_INST_KV(F16, 32) SATTN_INST_KV(F16, 64)
+SATTN_INST_KV2(Bf16) SATTN_INST_KV2(F16)
 #undef SATTN_INST
+#undef SATTN_INST_KV
+#undef SATTN_INST_KV2
 
 void launch_bwd_sparse(int dtype, int D, bool causal, const BwdParams& p, int64_t grid_q, int64_t grid_kv,
                    hipStream_t s) {

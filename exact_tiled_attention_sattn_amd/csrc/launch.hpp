@@ -38,6 +38,16 @@ constexpr int bwd_dq_waves(int D, bool causal, int layout) {
   return (D == 128 && !causal && layout == BWD_DENSE) ? 8 : 4;
 }
 
+// The dK/dV launch: at D = 128 the two-role kernel (8 waves, two per SIMD),
+// else the one-wave-per-key-block kernel (4 waves).
+template <class E, int D, bool CAUSAL, int LAYOUT>
+inline void launch_dkdv(const BwdParams& p, int64_t grid_kv, hipStream_t s) {
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((bwd_dkdv_roles_kernel<E, D, CAUSAL, LAYOUT>), dim3((unsigned)grid_kv), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);
+}
+
 // dtype: 0 = fp16, 1 = bf16 (the C ABI's sattn_dtype_t). D in {32, 64, 128}.
 void launch_fwd_dense(int dtype, int D, bool causal, const FwdParams& p, int64_t grid, hipStream_t s);
 // Small D <= 64 problems: `wide` selects 8 waves per workgroup, else 4.

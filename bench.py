@@ -39,6 +39,7 @@ Other modes:
 import argparse
 import csv
 import glob
+import gzip
 import hashlib
 import json
 import math
@@ -1083,10 +1084,12 @@ def load_traffic(src_hash):
 
 # ------------------------------------------------------------ profile summaries
 def _read_csv(pattern):
-    files = sorted(glob.glob(pattern, recursive=True))
+    """Rows of the first file matching ``pattern`` or ``pattern + '.gz'``."""
+    files = sorted(glob.glob(pattern, recursive=True) + glob.glob(pattern + ".gz", recursive=True))
     if not files:
         raise SystemExit("no file matches %s" % pattern)
-    with open(files[0]) as fh:
+    opener = gzip.open if files[0].endswith(".gz") else open
+    with opener(files[0], "rt") as fh:
         return list(csv.DictReader(fh)), files[0]
 
 
@@ -1259,10 +1262,10 @@ def pmc_summary(fetch_dir, write_dir, bench_logs, commands):
     for name, d, counter, run in (("fetch", fetch_dir, "FETCH_SIZE", lines[0]), ("write", write_dir, "WRITE_SIZE",
                                                                                  lines[1])):
         per = pers[name] = _counter_per_kernel(d, counter)
-        copies = [v for k_, vs in per.items() if "copyBuffer" in k_ for _, v in vs]
+        copies = sorted(x for k_, vs in per.items() if "copyBuffer" in k_ for x in vs)
         if not copies:
             raise SystemExit("no device copy kernel in the %s run" % counter)
-        cal_kib = max(copies)     # the 256 MiB calibration copy is the largest copy of the run
+        cal_kib = copies[0][1]    # the bench's 256 MiB calibration copy is the run's first device copy
         scale = (256 * 1024) / cal_kib
         res[name] = {"calibration_kib": cal_kib, "scale": scale}
         for tag, kname in HEADLINE_KERNELS.items():
@@ -1307,7 +1310,7 @@ def pmc_summary(fetch_dir, write_dir, bench_logs, commands):
         fb = statistics.median([v for _, v in pers["fetch"][kname]]) * res["fetch"]["scale"] * 1024
         wb = statistics.median([v for _, v in pers["write"][kname]]) * res["write"]["scale"] * 1024
         kn = _kname(kname)
-        what, ab = known.get(kn, (None, None))
+        what, ab = next((v for k_, v in known.items() if k_ in kn), (None, None))
         js["per_kernel"][kn] = {"dispatches": len(pers["fetch"][kname]), "fetch_bytes": fb, "write_bytes": wb,
                                 "algorithmic_bytes": ab, "workload": what}
         md.append("| `%s`%s | %d | %.1f | %.1f | %s | %s |" % (

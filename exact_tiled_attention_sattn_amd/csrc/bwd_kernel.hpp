@@ -42,7 +42,8 @@ struct BwdParams {
   int hq, hkv, n;
   int nk, off;          // dense layout: keys per slice and the position of query 0
                         // (Nk - Nq: queries are the last Nq tokens; 0 for equal lengths)
-  int nqt;              // dQ kernel: 128-query tiles per head (varlen: per longest sequence)
+  int nqt;              // dQ kernel: query tiles per head (varlen: per longest sequence)
+  int pair;             // dQ kernel, batched causal: workgroup j takes query tiles nqt-1-j and j
   int nkt;              // dK/dV kernel: 128-key tiles per KV head (varlen: per longest sequence)
   // varlen: q, o, dout, dq are [T, Hq, D] and k, v, dk, dv [T, Hkv, D]
   // packed tokens, lse and Delta [Hq, T]; sequence s owns tokens
@@ -122,212 +123,232 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[2 * TILE];
 
-  // block -> (query head, query tile); heaviest (causal: longest) query
-  // tiles first. Dense: heads contiguous per XCD. Varlen: KV head, then
-  // sequence, then query tile, then the query heads of the group, as in the
-  // varlen forward. Offsets in elements: qbase is row q_pos0 of q/o/dout/dq,
-  // kvbase key 0 of k/v, lbase row q_pos0 of lse/Delta.
-  // len: queries of the slice; klen: its keys; off: position of query 0
-  int len, klen, off = 0, q_pos0, qh;
-  int64_t qbase, kvbase, lbase, q_rs, kv_rs;
-  if constexpr (LAYOUT == BWD_VARLEN) {
-    const int grp = p.hq / p.hkv;
-    const int lin = xcd_linear(blockIdx.x);
-    const int per_g = p.nseq * p.nqt * grp;
-    const int g = lin / per_g;
-    const int r1 = lin % per_g;
-    const int sq = r1 / (p.nqt * grp);
-    const int r2 = r1 % (p.nqt * grp);
-    const int qt = p.nqt - 1 - r2 / grp;
-    const int h = g * grp + r2 % grp;
-    qh = h;
-    // clamp the table so that a malformed one cannot address outside [0, T)
-    int a = p.cu_seqlens[sq], e = p.cu_seqlens[sq + 1];
-    a = min(max(a, 0), p.total);
-    e = min(max(e, a), p.total);
-    len = e - a;
-    klen = len;
-    q_pos0 = qt * BM;
-    if (q_pos0 >= len) return;  // uniform over the workgroup
-    q_rs = (int64_t)p.hq * D;
-    kv_rs = (int64_t)p.hkv * D;
-    qbase = (int64_t)(a + q_pos0) * q_rs + (int64_t)h * D;
-    kvbase = (int64_t)a * kv_rs + (int64_t)g * D;
-    lbase = (int64_t)h * p.total + a + q_pos0;
-  } else {
-    const int lin = xcd_linear(blockIdx.x);
-    const int slice = lin / p.nqt;                 // b * Hq + h
-    const int qt = p.nqt - 1 - lin % p.nqt;
-    const int b = slice / p.hq, h = slice % p.hq;
-    const int kvs = b * p.hkv + h / (p.hq / p.hkv);
-    qh = h;
-    len = p.n;
-    klen = p.nk;
-    off = p.off;
-    q_pos0 = qt * BM;
-    q_rs = D;
-    kv_rs = D;
-    qbase = ((int64_t)slice * p.n + q_pos0) * D;
-    kvbase = (int64_t)kvs * p.nk * D;
-    lbase = (int64_t)slice * p.n + q_pos0;
-  }
-  const int nq = min(BM, len - q_pos0);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int l32 = lane & 31, hf = lane >> 5;
-  const int qrow = wave * 32 + l32;
-  const bool row_ok = qrow < nq;
-  const int my_pos = q_pos0 + off + qrow;
-  const bool wave_active = wave * 32 < nq;
-  const int wave_last_pos = q_pos0 + off + wave * 32 + 31;
-
-  // this lane's query row: Q and dO as MFMA B operands; Delta = dO . O
-  u32x4 qreg[KK], dreg[KK];
-  float delta = 0.f;
-  {
-    const int64_t off = qbase + (int64_t)qrow * q_rs + hf * 8;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      qreg[kk] = row_ok ? *(const u32x4*)(p.q + off + kk * 16) : u32x4{0, 0, 0, 0};
-      dreg[kk] = row_ok ? *(const u32x4*)(p.dout + off + kk * 16) : u32x4{0, 0, 0, 0};
-      const u32x4 ov = row_ok ? *(const u32x4*)(p.o + off + kk * 16) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        delta += E::lo(dreg[kk][j]) * E::lo(ov[j]) + E::hi(dreg[kk][j]) * E::hi(ov[j]);
-    }
-  }
-  delta = sum_halves(delta);
-  const float lse2 = row_ok ? p.lse[lbase + qrow] * kLog2e : 0.f;
-  if (row_ok && hf == 0) p.delta[lbase + qrow] = delta;
-
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-
-  const int k_end = CAUSAL ? min(klen, max(0, q_pos0 + off + BM)) : klen;
-  const int ntiles = (k_end + BN - 1) / BN;
-  const uint32_t row_bytes = (uint32_t)kv_rs * 2u;
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvbase), (short)0, (int)(k_end * row_bytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvbase), (short)0, (int)(k_end * row_bytes), 0x00020000);
-  TileLoader<D, NW> ld;
-  ld.init(wave, lane, row_bytes);
-  auto issue_tile = [&](int t, uint16_t* sb) {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(t * BN) * row_bytes);
-    ld.issue(rk, soff, sb, wave_u);
-    ld.issue(rv, soff, sb + TILE, wave_u);
-  };
-
-  int kofs[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) kofs[kk] = l32 * D + (((kk * 2 + hf) ^ swz<D>(l32)) * 8);
-  const int g16 = lane >> 4;
-  const int tr_key = 4 * (g16 >> 1) + ((lane & 15) >> 2);
-  int tofs[2][DB];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d0 = db * 32 + 16 * (g16 & 1) + 4 * (lane & 3);
-      const int key = tr_key + 8 * x;
-      tofs[x][db] = key * D + (((d0 >> 3) ^ swz<D>(key)) * 8) + (d0 & 7);
-    }
-
-  // Key tiles walked: [0, ntiles), or under the sparse operator (no global
-  // query among the rows) the global-key prefix [0, npre) and then the
-  // window band [band0, band0 + nsteps - npre).
-  int npre = 0, band0 = 0, nsteps = ntiles;
-  if constexpr (LAYOUT == BWD_SPARSE) {
-    if (q_pos0 >= p.n_global) {
-      npre = min(ntiles, (p.n_global + BN - 1) / BN);
-      const int lo = p.win_left < 0 ? 0 : max(0, q_pos0 - p.win_left) / BN;
-      const int hi = p.win_right < 0 ? ntiles : min(ntiles, (q_pos0 + BM - 1 + p.win_right) / BN + 1);
-      band0 = max(npre, lo);
-      nsteps = npre + max(0, hi - band0);
-    }
-  }
-  auto tile_of = [&](int idx) { return idx < npre ? idx : band0 + (idx - npre); };
-
-  auto step = [&](int idx, const uint16_t* cur, uint16_t* nxt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (idx + 1 < nsteps) issue_tile(tile_of(idx + 1), nxt);
-    const int kt0 = tile_of(idx) * BN;
-    if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
-    bool edge = kt0 + BN > klen || (CAUSAL && kt0 + BN - 1 > q_pos0 + off + wave * 32);
-    if constexpr (LAYOUT == BWD_SPARSE) {
-      // the wave's 32 rows lie in one mask row block and the tile's keys in
-      // one key block (block_q % 32 == 0, block_k % 64 == 0)
-      const int i0 = q_pos0 + wave_u * 32, i1 = min(i0 + 31, len - 1);
-      const int j1 = min(kt0 + BN, klen) - 1;
-      if (!sparse_bit(p, qh, i0, kt0) || !sparse_any(p, i0, i1, kt0, j1)) return;
-      edge = edge || !sparse_all(p, i0, i1, kt0, j1);
-    }
-    const uint16_t* sK = cur;
-    const uint16_t* sV = cur + TILE;
-    // S^T = K Q^T and dP^T = V dO^T (keys x queries, one query per lane)
-    f32x16 s[KB], dp[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = 0.f;
-        dp[kb][r] = 0.f;
+  // One query tile of a workgroup (two for batched causal pairs).
+  auto run_item = [&](int item) {
+    // block -> (query head, query tile); heaviest (causal: longest) query
+    // tiles first. Dense: heads contiguous per XCD. Varlen: KV head, then
+    // sequence, then query tile, then the query heads of the group, as in the
+    // varlen forward. Offsets in elements: qbase is row q_pos0 of q/o/dout/dq,
+    // kvbase key 0 of k/v, lbase row q_pos0 of lse/Delta.
+    // len: queries of the slice; klen: its keys; off: position of query 0
+    int len, klen, off = 0, q_pos0, qh;
+    int64_t qbase, kvbase, lbase, q_rs, kv_rs;
+    if constexpr (LAYOUT == BWD_VARLEN) {
+      const int grp = p.hq / p.hkv;
+      const int lin = xcd_linear(blockIdx.x);
+      const int per_g = p.nseq * p.nqt * grp;
+      const int g = lin / per_g;
+      const int r1 = lin % per_g;
+      const int sq = r1 / (p.nqt * grp);
+      const int r2 = r1 % (p.nqt * grp);
+      const int qt = p.nqt - 1 - r2 / grp;
+      const int h = g * grp + r2 % grp;
+      qh = h;
+      // clamp the table so that a malformed one cannot address outside [0, T)
+      int a = p.cu_seqlens[sq], e = p.cu_seqlens[sq + 1];
+      a = min(max(a, 0), p.total);
+      e = min(max(e, a), p.total);
+      len = e - a;
+      klen = len;
+      q_pos0 = qt * BM;
+      if (q_pos0 >= len) return;  // uniform over the workgroup
+      q_rs = (int64_t)p.hq * D;
+      kv_rs = (int64_t)p.hkv * D;
+      qbase = (int64_t)(a + q_pos0) * q_rs + (int64_t)h * D;
+      kvbase = (int64_t)a * kv_rs + (int64_t)g * D;
+      lbase = (int64_t)h * p.total + a + q_pos0;
+    } else {
+      // batched causal pairs: item 0 the longer tile nqt-1-j, item 1 tile j
+      const int lin = xcd_linear(blockIdx.x);
+      int slice, qt;
+      if (CAUSAL && p.pair) {
+        const int npairs = (p.nqt + 1) / 2;
+        slice = lin / npairs;
+        const int j = lin % npairs;
+        qt = item == 0 ? p.nqt - 1 - j : j;
+        if (item == 1 && qt == p.nqt - 1 - j) return;   // odd count: the middle tile once
+      } else {
+        if (item > 0) return;
+        slice = lin / p.nqt;   // b * Hq + h
+        qt = p.nqt - 1 - lin % p.nqt;
       }
-#pragma unroll
+      const int b = slice / p.hq, h = slice % p.hq;
+      const int kvs = b * p.hkv + h / (p.hq / p.hkv);
+      qh = h;
+      len = p.n;
+      klen = p.nk;
+      off = p.off;
+      q_pos0 = qt * BM;
+      q_rs = D;
+      kv_rs = D;
+      qbase = ((int64_t)slice * p.n + q_pos0) * D;
+      kvbase = (int64_t)kvs * p.nk * D;
+      lbase = (int64_t)slice * p.n + q_pos0;
+    }
+    const int nq = min(BM, len - q_pos0);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int qrow = wave * 32 + l32;
+    const bool row_ok = qrow < nq;
+    const int my_pos = q_pos0 + off + qrow;
+    const bool wave_active = wave * 32 < nq;
+    const int wave_last_pos = q_pos0 + off + wave * 32 + 31;
+
+    // this lane's query row: Q and dO as MFMA B operands; Delta = dO . O
+    u32x4 qreg[KK], dreg[KK];
+    float delta = 0.f;
+    {
+      const int64_t off = qbase + (int64_t)qrow * q_rs + hf * 8;
+  #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s[kb] = E::mfma32(*(const u32x4*)(sK + kofs[kk] + kb * 32 * D), qreg[kk], s[kb]);
-        dp[kb] = E::mfma32(*(const u32x4*)(sV + kofs[kk] + kb * 32 * D), dreg[kk], dp[kb]);
+        qreg[kk] = row_ok ? *(const u32x4*)(p.q + off + kk * 16) : u32x4{0, 0, 0, 0};
+        dreg[kk] = row_ok ? *(const u32x4*)(p.dout + off + kk * 16) : u32x4{0, 0, 0, 0};
+        const u32x4 ov = row_ok ? *(const u32x4*)(p.o + off + kk * 16) : u32x4{0, 0, 0, 0};
+  #pragma unroll
+        for (int j = 0; j < 4; ++j)
+          delta += E::lo(dreg[kk][j]) * E::lo(ov[j]) + E::hi(dreg[kk][j]) * E::hi(ov[j]);
       }
     }
-    // P = exp2(S c - lse log2 e) on eligible keys; dS = P (dP - Delta)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(fmaf(s[kb][r], p.c, -lse2));
-        if (edge) {
-          const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= klen || (CAUSAL && key > my_pos) || (LAYOUT == BWD_SPARSE && !sparse_pair(p, my_pos, key)))
-            pr = 0.f;
-        }
-        s[kb][r] = pr * (dp[kb][r] - delta);
+    delta = sum_halves(delta);
+    const float lse2 = row_ok ? p.lse[lbase + qrow] * kLog2e : 0.f;
+    if (row_ok && hf == 0) p.delta[lbase + qrow] = delta;
+
+    f32x16 acc[DB];
+  #pragma unroll
+    for (int db = 0; db < DB; ++db)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    const int k_end = CAUSAL ? min(klen, max(0, q_pos0 + off + BM)) : klen;
+    const int ntiles = (k_end + BN - 1) / BN;
+    const uint32_t row_bytes = (uint32_t)kv_rs * 2u;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvbase), (short)0, (int)(k_end * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvbase), (short)0, (int)(k_end * row_bytes), 0x00020000);
+    TileLoader<D, NW> ld;
+    ld.init(wave, lane, row_bytes);
+    auto issue_tile = [&](int t, uint16_t* sb) {
+      const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(t * BN) * row_bytes);
+      ld.issue(rk, soff, sb, wave_u);
+      ld.issue(rv, soff, sb + TILE, wave_u);
+    };
+
+    int kofs[KK];
+  #pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kofs[kk] = l32 * D + (((kk * 2 + hf) ^ swz<D>(l32)) * 8);
+    const int g16 = lane >> 4;
+    const int tr_key = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+    int tofs[2][DB];
+  #pragma unroll
+    for (int x = 0; x < 2; ++x)
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d0 = db * 32 + 16 * (g16 & 1) + 4 * (lane & 3);
+        const int key = tr_key + 8 * x;
+        tofs[x][db] = key * D + (((d0 >> 3) ^ swz<D>(key)) * 8) + (d0 & 7);
       }
-    // dQ^T += K^T dS^T (16 keys per MFMA; K^T by transposing reads)
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int o8 = half * 8;
-        const u32x4 pb = {E::pack2(s[kb][o8 + 0], s[kb][o8 + 1]), E::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
-                          E::pack2(s[kb][o8 + 4], s[kb][o8 + 5]), E::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
-        const int krow = (kb * 32 + half * 16) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x2 a0 = lds_read_tr16(sK + tofs[0][db] + krow);
-          const u32x2 a1 = lds_read_tr16(sK + tofs[1][db] + krow);
-          acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, acc[db]);
+
+    // Key tiles walked: [0, ntiles), or under the sparse operator (no global
+    // query among the rows) the global-key prefix [0, npre) and then the
+    // window band [band0, band0 + nsteps - npre).
+    int npre = 0, band0 = 0, nsteps = ntiles;
+    if constexpr (LAYOUT == BWD_SPARSE) {
+      if (q_pos0 >= p.n_global) {
+        npre = min(ntiles, (p.n_global + BN - 1) / BN);
+        const int lo = p.win_left < 0 ? 0 : max(0, q_pos0 - p.win_left) / BN;
+        const int hi = p.win_right < 0 ? ntiles : min(ntiles, (q_pos0 + BM - 1 + p.win_right) / BN + 1);
+        band0 = max(npre, lo);
+        nsteps = npre + max(0, hi - band0);
+      }
+    }
+    auto tile_of = [&](int idx) { return idx < npre ? idx : band0 + (idx - npre); };
+
+    auto step = [&](int idx, const uint16_t* cur, uint16_t* nxt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (idx + 1 < nsteps) issue_tile(tile_of(idx + 1), nxt);
+      const int kt0 = tile_of(idx) * BN;
+      if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
+      bool edge = kt0 + BN > klen || (CAUSAL && kt0 + BN - 1 > q_pos0 + off + wave * 32);
+      if constexpr (LAYOUT == BWD_SPARSE) {
+        // the wave's 32 rows lie in one mask row block and the tile's keys in
+        // one key block (block_q % 32 == 0, block_k % 64 == 0)
+        const int i0 = q_pos0 + wave_u * 32, i1 = min(i0 + 31, len - 1);
+        const int j1 = min(kt0 + BN, klen) - 1;
+        if (!sparse_bit(p, qh, i0, kt0) || !sparse_any(p, i0, i1, kt0, j1)) return;
+        edge = edge || !sparse_all(p, i0, i1, kt0, j1);
+      }
+      const uint16_t* sK = cur;
+      const uint16_t* sV = cur + TILE;
+      // S^T = K Q^T and dP^T = V dO^T (keys x queries, one query per lane)
+      f32x16 s[KB], dp[KB];
+  #pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[kb][r] = 0.f;
+          dp[kb][r] = 0.f;
+        }
+  #pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          s[kb] = E::mfma32(*(const u32x4*)(sK + kofs[kk] + kb * 32 * D), qreg[kk], s[kb]);
+          dp[kb] = E::mfma32(*(const u32x4*)(sV + kofs[kk] + kb * 32 * D), dreg[kk], dp[kb]);
         }
       }
+      // P = exp2(S c - lse log2 e) on eligible keys; dS = P (dP - Delta)
+  #pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = fast_exp2(fmaf(s[kb][r], p.c, -lse2));
+          if (edge) {
+            const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key >= klen || (CAUSAL && key > my_pos) || (LAYOUT == BWD_SPARSE && !sparse_pair(p, my_pos, key)))
+              pr = 0.f;
+          }
+          s[kb][r] = pr * (dp[kb][r] - delta);
+        }
+      // dQ^T += K^T dS^T (16 keys per MFMA; K^T by transposing reads)
+  #pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int o8 = half * 8;
+          const u32x4 pb = {E::pack2(s[kb][o8 + 0], s[kb][o8 + 1]), E::pack2(s[kb][o8 + 2], s[kb][o8 + 3]),
+                            E::pack2(s[kb][o8 + 4], s[kb][o8 + 5]), E::pack2(s[kb][o8 + 6], s[kb][o8 + 7])};
+          const int krow = (kb * 32 + half * 16) * D;
+  #pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x2 a0 = lds_read_tr16(sK + tofs[0][db] + krow);
+            const u32x2 a1 = lds_read_tr16(sK + tofs[1][db] + krow);
+            acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb, acc[db]);
+          }
+        }
+    };
+    if (nsteps > 0) {
+      issue_tile(tile_of(0), sbuf0);
+      int t = 0;
+      for (; t + 1 < nsteps; t += 2) {
+        step(t, sbuf0, sbuf1);
+        step(t + 1, sbuf1, sbuf0);
+      }
+      if (t < nsteps) step(t, sbuf0, sbuf1);
+    }
+    // dQ leaves through the idle tile buffers as whole rows (waves 0-3 in
+    // sbuf0, 4-7 in sbuf1), once every wave is done with them
+    __syncthreads();
+    store_tile_rows<E, D>(acc, p.scale, (wave_u < 4 ? sbuf0 : sbuf1) + (wave_u & 3) * 32 * D,
+                          p.dq + qbase + (int64_t)wave_u * 32 * q_rs, q_rs, nq - wave_u * 32);
   };
-  if (nsteps > 0) {
-    issue_tile(tile_of(0), sbuf0);
-    int t = 0;
-    for (; t + 1 < nsteps; t += 2) {
-      step(t, sbuf0, sbuf1);
-      step(t + 1, sbuf1, sbuf0);
-    }
-    if (t < nsteps) step(t, sbuf0, sbuf1);
+  constexpr int NITEMS = (LAYOUT == BWD_DENSE && CAUSAL) ? 2 : 1;
+#pragma unroll 1
+  for (int item = 0; item < NITEMS; ++item) {
+    if (item > 0) __syncthreads();   // every wave is done with the previous tile's buffers
+    run_item(item);
   }
-  // dQ leaves through the idle tile buffers as whole rows (waves 0-3 in
-  // sbuf0, 4-7 in sbuf1), once every wave is done with them
-  __syncthreads();
-  store_tile_rows<E, D>(acc, p.scale, (wave_u < 4 ? sbuf0 : sbuf1) + (wave_u & 3) * 32 * D,
-                        p.dq + qbase + (int64_t)wave_u * 32 * q_rs, q_rs, nq - wave_u * 32);
 }
 
 // Work of one dK/dV workgroup: up to 128 keys of one KV head, and the walk

@@ -33,9 +33,10 @@ constexpr int kDenseBN = SATTN_DENSE_BN;
 constexpr int kCacheWideRows = 512;
 
 // Waves of the backward dQ kernel: 8 (256 queries per workgroup) for the
-// non-causal batched layout at D = 128, else 4.
+// batched layout at D = 128 (causal grids of enough tiles then pair their
+// query tiles, as the forward does), else 4.
 constexpr int bwd_dq_waves(int D, bool causal, int layout) {
-  return (D == 128 && !causal && layout == BWD_DENSE) ? 8 : 4;
+  return (D == 128 && layout == BWD_DENSE) ? 8 : 4;
 }
 
 // The dK/dV launch: at D = 128 the two-role kernel (8 waves, two per SIMD),

@@ -517,7 +517,10 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
   p.nkt = (int)((Nk + 127) / 128);
   p.c = scale * kLog2e;
   p.scale = scale;
-  const int64_t grid_q = B * Hq * p.nqt, grid_kv = B * Hkv * p.nkt;  // dQ: BM = bmq rows per workgroup
+  // dQ: BM = bmq rows per workgroup; batched causal grids of at least 1024
+  // query tiles pair them (tiles nqt-1-j and j per workgroup)
+  p.pair = (!sp && causal && bmq == 256 && B * Hq * p.nqt >= 1024) ? 1 : 0;
+  const int64_t grid_q = B * Hq * (p.pair ? (p.nqt + 1) / 2 : p.nqt), grid_kv = B * Hkv * p.nkt;
   if (grid_q >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
   if (sp) {
     p.win_left = (int)sp->left;

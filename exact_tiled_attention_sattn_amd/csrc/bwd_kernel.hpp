@@ -11,12 +11,12 @@
 // Two kernels, no atomics, every sum in a fixed order:
 //   bwd_dq_kernel   -- a wave owns 32 queries and walks 64-key K/V tiles
 //                      (the forward's walk); it also forms Delta and stores it.
-//   bwd_dkdv_roles_kernel (D = 128) -- two waves of one SIMD own 32 keys
+//   bwd_dkdv_roles_kernel (D = 128; causal D = 64) -- two waves of one SIMD own 32 keys
 //                      and walk 64-query Q/dO tiles of every query head of
 //                      their KV head, one forming P and dV, the other dP, dS
 //                      and dK; it runs after the dQ kernel on the same stream
 //                      and reads Delta.
-//   bwd_dkdv_kernel (D = 32, 64) -- the same walk, one wave per 32 keys
+//   bwd_dkdv_kernel (D = 32; non-causal D = 64) -- the same walk, one wave per 32 keys
 //                      forming both.
 // MFMA operand layouts follow the forward: a lane owns one row of the 32x32
 // accumulator's columns; operands of the transposed products come from
@@ -722,7 +722,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_roles_kernel(const BwdParams 
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int TILE = BMQ * D;                 // elements of one Q or dO tile
   constexpr int BUF = 2 * TILE + 2 * BMQ * 2;   // Q, dO, then lse and Delta (fp32)
-  static_assert(D == 128, "two-role layout: 8 waves of 32 keys, D = 128");
+  static_assert(D == 64 || D == 128, "two-role layout: 8 waves of 32 keys, D = 64 or 128");
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf0[BUF];
   __shared__ __attribute__((aligned(1024))) uint16_t sbuf1[BUF];
   // P of the current step: [key block][32-query block][register group][lane]

@@ -22,20 +22,23 @@ void go(bool causal, const BwdParams& p, int64_t grid_q, int64_t grid_kv, hipStr
 
 // Explicit instantiations, so that every kernel of this layout has its
 // device code and host stub in this object: dQ for every D; dK/dV in two
-// roles at D = 128, one wave per key block below.
+// roles where bwd_dkdv_roles says so, else one wave per key block.
 #define SATTN_INST(E_, D_)                                                                      \
   template __global__ void bwd_dq_kernel<E_, D_, true, BWD_VARLEN, bwd_dq_waves(D_, true, BWD_VARLEN)>(const BwdParams);  \
   template __global__ void bwd_dq_kernel<E_, D_, false, BWD_VARLEN, bwd_dq_waves(D_, false, BWD_VARLEN)>(const BwdParams);
 #define SATTN_INST_KV(E_, D_)                                                         \
   template __global__ void bwd_dkdv_kernel<E_, D_, true, BWD_VARLEN>(const BwdParams);  \
   template __global__ void bwd_dkdv_kernel<E_, D_, false, BWD_VARLEN>(const BwdParams);
-#define SATTN_INST_KV2(E_)                                                                 \
-  template __global__ void bwd_dkdv_roles_kernel<E_, 128, true, BWD_VARLEN>(const BwdParams);  \
-  template __global__ void bwd_dkdv_roles_kernel<E_, 128, false, BWD_VARLEN>(const BwdParams);
+#define SATTN_INST_KV2(E_, D_)                                                                 \
+  template __global__ void bwd_dkdv_roles_kernel<E_, D_, true, BWD_VARLEN>(const BwdParams);  \
+  template __global__ void bwd_dkdv_roles_kernel<E_, D_, false, BWD_VARLEN>(const BwdParams);
 SATTN_INST(Bf16, 32) SATTN_INST(Bf16, 64) SATTN_INST(Bf16, 128)
 SATTN_INST(F16, 32) SATTN_INST(F16, 64) SATTN_INST(F16, 128)
-SATTN_INST_KV(Bf16, 32) SATTN_INST_KV(Bf16, 64) SATTN_INST_KV(F16, 32) SATTN_INST_KV(F16, 64)
-SATTN_INST_KV2(Bf16) SATTN_INST_KV2(F16)
+SATTN_INST_KV(Bf16, 32) SATTN_INST_KV(F16, 32) SATTN_INST_KV2(Bf16, 128) SATTN_INST_KV2(F16, 128)
+template __global__ void bwd_dkdv_kernel<Bf16, 64, false, BWD_VARLEN>(const BwdParams);
+template __global__ void bwd_dkdv_kernel<F16, 64, false, BWD_VARLEN>(const BwdParams);
+template __global__ void bwd_dkdv_roles_kernel<Bf16, 64, true, BWD_VARLEN>(const BwdParams);
+template __global__ void bwd_dkdv_roles_kernel<F16, 64, true, BWD_VARLEN>(const BwdParams);
 #undef SATTN_INST
 #undef SATTN_INST_KV
 #undef SATTN_INST_KV2

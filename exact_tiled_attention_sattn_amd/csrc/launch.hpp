@@ -39,11 +39,14 @@ constexpr int bwd_dq_waves(int D, bool causal, int layout) {
   return (D == 128 && layout == BWD_DENSE) ? 8 : 4;
 }
 
-// The dK/dV launch: at D = 128 the two-role kernel (8 waves, two per SIMD),
-// else the one-wave-per-key-block kernel (4 waves).
+// Whether dK/dV runs in two roles per SIMD (8 waves) rather than one wave
+// per 32 keys (4 waves): at D = 128, and causal at D = 64 (non-causal D = 64
+// measured 1.4% slower in two roles, causal 7.9% faster).
+constexpr bool bwd_dkdv_roles(int D, bool causal) { return D == 128 || (D == 64 && causal); }
+
 template <class E, int D, bool CAUSAL, int LAYOUT>
 inline void launch_dkdv(const BwdParams& p, int64_t grid_kv, hipStream_t s) {
-  if constexpr (D == 128)
+  if constexpr (bwd_dkdv_roles(D, CAUSAL))
     hipLaunchKernelGGL((bwd_dkdv_roles_kernel<E, D, CAUSAL, LAYOUT>), dim3((unsigned)grid_kv), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, CAUSAL, LAYOUT>), dim3((unsigned)grid_kv), dim3(256), 0, s, p);

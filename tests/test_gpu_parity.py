@@ -1160,6 +1160,13 @@ def test_backward_batched_4x16x4096x128_bf16_two_heads():
                                            W.to_f64(do[bi, hi]), scale, True)
         _check_grads((dq[sl], dk[sl], dv[sl]), tuple(r[None, None] for r in refs), q[sl], k[sl], v[sl], do[sl],
                      o[sl], scale, True, torch.bfloat16, "[%d,%d] " % (bi, hi))
+        # This grid pairs its dQ query tiles (tiles nqt-1-j and j per
+        # workgroup); one slice alone runs unpaired. The gradients of the
+        # slice do not depend on which tiles share a workgroup.
+        one = sattn_bwd(*(x[sl].contiguous() for x in (qd, kd, vd, o, dod)), lse[sl].contiguous(), causal=True,
+                        scale=scale)
+        for a, b_, name in zip((dq[sl], dk[sl], dv[sl]), one, ("dq", "dk", "dv")):
+            assert torch.equal(a, b_), "[%d,%d] %s of the batched call differs from the slice alone" % (bi, hi, name)
 
 
 @pytest.mark.parametrize("growth", [3.0, 50.0])

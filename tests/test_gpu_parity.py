@@ -242,6 +242,27 @@ def test_split_matches_fwd():
     assert (l1 - l2).abs().max().item() <= 1e-3
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_merge_many_chunks(d):
+    """150 partials per row (the weights are taken 64 chunks at a time and
+    the partial rows loaded 16 at a time): a row with every partial empty but
+    the last, one with a whole group of 64 empty, and rows whose maximum sits
+    in the last, ragged group."""
+    _banner("merge many chunks", d)
+    rows, c = 9, 150
+    g = torch.Generator().manual_seed(150 + d)
+    pm = torch.randn(rows, c, generator=g) * 4
+    pl = torch.rand(rows, c, generator=g) * 50 + 1
+    pa = torch.randn(rows, c, d, generator=g) * 3
+    pm[0, :-1] = -float("inf"); pl[0, :-1] = 0; pa[0, :-1] = 0
+    pm[1, 64:128] = -float("inf"); pl[1, 64:128] = 0; pa[1, 64:128] = 0
+    pm[2:5, 140] += 20.0
+    o, lse = sattn_merge(pm.to(DEV), pl.to(DEV), pa.to(DEV), torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = dense.merge_partials(pm.double().numpy(), pl.double().numpy(), pa.double().numpy())
+    check_attention(o, lse, o_ref, lse_ref, torch.bfloat16, "merge many chunks")
+
+
 def test_merge_empty_partials_identity():
     """Empty partials (m=-inf, l=0, acc=0) change nothing; all-empty rows give
     O = 0, lse = -inf."""

@@ -800,6 +800,8 @@ SPARSE = [
     (1, 4, 2, 1000, 1000, 64, "fp16", True, 300, -1, 0, (1, 128, 128)),  # shared mask + causal window
     (1, 2, 1, 200, 900, 128, "bf16", True, 256, -1, 0, None),       # cache alignment, Nq < Nk
     (1, 2, 2, 333, 333, 32, "fp16", True, 17, 2, 1, (2, 32, 64)),   # small blocks, ragged
+    (1, 2, 1, 700, 700, 128, "fp16", True, 300, -1, 4, (2, 64, 128)),  # 64-row blocks: 64-row workgroups
+    (1, 2, 2, 500, 800, 128, "bf16", True, -1, -1, 0, (1, 96, 64)),    # 96-row blocks, cache alignment
 ]
 
 

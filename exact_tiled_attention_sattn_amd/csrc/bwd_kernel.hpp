@@ -482,10 +482,9 @@ struct KvWalk {
 // ---------------------------------------------------------------- dK, dV
 template <class E, int D, bool CAUSAL, int LAYOUT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
-  constexpr bool VARLEN = LAYOUT == BWD_VARLEN;
   constexpr bool SPARSE = LAYOUT == BWD_SPARSE;
-  // queries per step, in 64-row sub-tiles (128 measured no faster)
-  constexpr int NW = 4, BNK = 128, BMQ = 64;
+  // queries per step, in 64-row sub-tiles (128 measured no faster); 128 keys per workgroup (KvWalk)
+  constexpr int NW = 4, BMQ = 64;
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int TILE = BMQ * D;                 // elements of one Q or dO tile
   constexpr int BUF = 2 * TILE + 2 * BMQ * 2;   // Q, dO, then lse and Delta (fp32)
@@ -494,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 
   KvWalk<D, CAUSAL, LAYOUT> wk;
   if (!wk.init(p)) return;   // uniform over the workgroup
-  const int grp = wk.grp, len = wk.len, qlen = wk.qlen, off = wk.off, k0 = wk.k0, g = wk.g;
+  const int len = wk.len, qlen = wk.qlen, off = wk.off, k0 = wk.k0;
   const int64_t kvbase = wk.kvbase, kv_rs = wk.kv_rs;
   const int nkeys = wk.nkeys;
 
@@ -716,9 +715,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const BwdParams p) {
 // kernel's (bwd_dkdv_kernel), bit for bit.
 template <class E, int D, bool CAUSAL, int LAYOUT>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_roles_kernel(const BwdParams p) {
-  constexpr bool VARLEN = LAYOUT == BWD_VARLEN;
   constexpr bool SPARSE = LAYOUT == BWD_SPARSE;
-  constexpr int NW = 8, BNK = 128, BMQ = 64;
+  constexpr int NW = 8, BMQ = 64;   // 128 keys per workgroup (KvWalk)
   constexpr int KK = D / 16, DB = D / 32;
   constexpr int TILE = BMQ * D;                 // elements of one Q or dO tile
   constexpr int BUF = 2 * TILE + 2 * BMQ * 2;   // Q, dO, then lse and Delta (fp32)
@@ -730,7 +728,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_roles_kernel(const BwdParams 
 
   KvWalk<D, CAUSAL, LAYOUT> wk;
   if (!wk.init(p)) return;   // uniform over the workgroup
-  const int grp = wk.grp, len = wk.len, qlen = wk.qlen, off = wk.off, k0 = wk.k0, g = wk.g;
+  const int len = wk.len, qlen = wk.qlen, off = wk.off, k0 = wk.k0;
   const int64_t kvbase = wk.kvbase, kv_rs = wk.kv_rs;
   const int nkeys = wk.nkeys;
 

@@ -1244,13 +1244,13 @@ def sq_summary(sq_dir, bench_log, command):
     return "\n".join(md) + "\n"
 
 
-def pmc_summary(fetch_dir, write_dir, bench_logs, commands):
+def pmc_summary(fetch_dir, write_dir, bench_logs, commands, out=PMC_SUMMARY):
     """HBM traffic of the headline kernels from FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled by what the same counter reads for the
     bench's plain 256 MiB device copy; medians over the timed dispatches.
     Each counter comes from a bench run of its own, whose log (in the order
     FETCH_SIZE, WRITE_SIZE) says which dispatches were timed. Writes the
-    committed summary (.md and .json)."""
+    committed summary (.md and .json; ``out`` names the .json)."""
     if len(bench_logs) != 2:
         raise SystemExit("--pmc-summary needs two --bench-log files: the FETCH_SIZE run's, then the WRITE_SIZE run's")
     lines = [_bench_line(b) for b in bench_logs]
@@ -1316,7 +1316,7 @@ def pmc_summary(fetch_dir, write_dir, bench_logs, commands):
         md.append("| `%s`%s | %d | %.1f | %.1f | %s | %s |" % (
             _disp(kname), (" (%s)" % what) if what else "", len(pers["fetch"][kname]), fb / 1e6,
             wb / 1e6, "%.1f" % (ab / 1e6) if ab else "", "%.2f" % ((fb + wb) / ab) if ab else ""))
-    base = os.path.splitext(PMC_SUMMARY)[0]
+    base = os.path.splitext(out)[0]
     with open(base + ".json", "w") as fh:
         json.dump(js, fh, indent=1)
     with open(base + ".md", "w") as fh:

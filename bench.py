@@ -62,6 +62,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 KERNEL_SOURCES = ["exact_tiled_attention_sattn_amd/csrc/fwd_kernel.hpp",
                   "exact_tiled_attention_sattn_amd/csrc/common.hpp",
                   "exact_tiled_attention_sattn_amd/csrc/fwd_small.hpp",
+                  "exact_tiled_attention_sattn_amd/csrc/fwd_decode.hpp",
                   "exact_tiled_attention_sattn_amd/csrc/launch.hpp",
                   "exact_tiled_attention_sattn_amd/csrc/k_fwd_dense.hip",
                   "exact_tiled_attention_sattn_amd/csrc/sattn.hip"]
@@ -1188,7 +1189,7 @@ def _counter_per_kernel(d, counter):
 # (workload, kernel, (extras leg, key)). The chunk-width sweep launches the
 # split kernel at other widths too; those read the same K/V bytes.
 EXTRA_TRAFFIC = [
-    ("split-KV decode partials 16x32x131072x128 bf16", "fwd_kernel<Bf16, 128, 64, 4, false, 2>",
+    ("split-KV decode partials 16x32x131072x128 bf16", "split_row_kernel<Bf16, 128, false>",
      ("splitkv_decode", "algorithmic_bytes_split")),
     ("causal GQA decode partials, 4 q vs 32768 cached, B=8, 32q/8kv", "fwd_kernel<Bf16, 128, 64, 4, true, 2>",
      ("cache_gqa_decode", "algorithmic_bytes_split")),

@@ -1,11 +1,16 @@
 // Split-KV partial states (optionally causal, cache alignment) and their merge.
 #include "launch.hpp"
+#include "fwd_decode.hpp"
 
 namespace sattn {
 
 namespace {
 template <class E, int D, bool CAUSAL>
 void go(const FwdParams& p, int64_t grid, hipStream_t s) {
+  if (p.n == 1 && !p.pack) {   // one row per slice: the grid is (row, chunk) already
+    hipLaunchKernelGGL((split_row_kernel<E, D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    return;
+  }
   constexpr int NW = Tile<D, MODE_SPLIT>::NW;
   hipLaunchKernelGGL((fwd_kernel<E, D, 64, NW, CAUSAL, MODE_SPLIT>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
 }

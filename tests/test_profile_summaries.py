@@ -14,7 +14,7 @@ import bench
 
 NC = "void sattn::fwd_kernel<sattn::Bf16, 128, 64, 8, false, 0>(sattn::FwdParams)"
 CA = "void sattn::fwd_kernel<sattn::Bf16, 128, 64, 8, true, 0>(sattn::FwdParams)"
-SPLIT = "void sattn::fwd_kernel<sattn::Bf16, 128, 64, 4, false, 2>(sattn::FwdParams)"
+SPLIT = "void sattn::split_row_kernel<sattn::Bf16, 128, false>(sattn::FwdParams)"
 COPY = "__amd_rocclr_copyBuffer"
 
 

@@ -205,6 +205,13 @@ SPLIT_SMALL = [
     (1, 1, 1, 40, 130, 32, 64, "fp16"),
     (1, 2, 1, 1, 50, 128, 4096, "bf16"),       # one chunk larger than Nk
     (1, 1, 1, 2, 65, 64, 1, "bf16"),           # one key per chunk
+    # one query row per slice (the vector-unit row kernel): ragged last
+    # chunks, chunks too short to give every wave keys, one key per chunk
+    (2, 3, 3, 1, 1000, 32, 96, "fp16"),
+    (1, 2, 2, 1, 777, 64, 200, "bf16"),
+    (1, 1, 1, 1, 5, 128, 4096, "fp16"),
+    (1, 2, 2, 1, 300, 128, 1, "bf16"),
+    (1, 2, 2, 1, 4099, 128, 1030, "fp16"),
 ]
 
 
@@ -227,6 +234,30 @@ def test_split_partials_and_merge_small(b, hq, hkv, nq, nk, d, chunk, dt):
             check_lse(pm_[bb, h] + np.log(pl_[bb, h]), m_ref + np.log(l_ref), "partial lse")
             check_o(pa_[bb, h] / pl_[bb, h][..., None], a_ref / l_ref[..., None], W.DTYPES[dt], "partial o")
             o_ref, lse_ref = dense.attention(qf[bb, h], kf[bb, h // g], vf[bb, h // g], scale)
+            check_attention(o[bb, h], lse[bb, h], o_ref, lse_ref, W.DTYPES[dt], "merged")
+
+
+@pytest.mark.parametrize("d,dt", [(128, "bf16"), (64, "fp16")])
+def test_split_row_large_logits(d, dt):
+    """One query row per slice with Q x 16 (score spread of about 16 nats):
+    the row kernel's running maximum changes many times within a chunk."""
+    _banner("split row large logits", d, dt)
+    q, k, v = W.qkv((2, 2, 1, d), (2, 2, 3000, d), dt, seed=2600 + d)
+    q = q * 16
+    scale = W.scale_f32(d)
+    chunk = 512
+    pm, pl, pa = sattn_fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), chunk, scale)
+    o, lse = sattn_merge(pm, pl, pa, W.DTYPES[dt])
+    torch.cuda.synchronize()
+    qf, kf, vf = W.to_f64(q), W.to_f64(k), W.to_f64(v)
+    pm_, pl_, pa_ = (x.cpu().double().numpy() for x in (pm, pl, pa))
+    for bb in range(2):
+        for h in range(2):
+            m_ref, l_ref, a_ref = dense.split_partials(qf[bb, h], kf[bb, h], vf[bb, h], scale, chunk)
+            np.testing.assert_allclose(pm_[bb, h], m_ref, rtol=0, atol=1e-3 * max(1.0, np.abs(m_ref).max()))
+            check_lse(pm_[bb, h] + np.log(pl_[bb, h]), m_ref + np.log(l_ref), "partial lse")
+            check_o(pa_[bb, h] / pl_[bb, h][..., None], a_ref / l_ref[..., None], W.DTYPES[dt], "partial o")
+            o_ref, lse_ref = dense.attention(qf[bb, h], kf[bb, h], vf[bb, h], scale)
             check_attention(o[bb, h], lse[bb, h], o_ref, lse_ref, W.DTYPES[dt], "merged")
 
 
@@ -694,6 +725,7 @@ SPLIT_CACHE_SMALL = [
     (1, 8, 2, 5, 333, 128, 64, "bf16"),
     (2, 6, 2, 40, 500, 64, 128, "fp16"),     # 120 rows per slice over two 64-row tiles
     (1, 4, 1, 64, 64, 32, 32, "bf16"),       # every row's own chunk cut at its position
+    (1, 2, 2, 1, 300, 64, 64, "bf16"),       # one row per slice (the row kernel), causal
 ]
 
 

@@ -76,8 +76,9 @@ const char* sattn_last_error(void);
 
 /*
  * Batched multi-head attention forward ("Intermediate and advanced
- * extension", workshop table, streaming-attention row: tile QK and PV with
- * online rescaling, causal and noncausal self-attention).
+ * extension", workshop table, streaming-attention row: the score and value
+ * products taken tile by tile under a running rescale, with or without the
+ * causal mask).
  *
  *   q, k, v, o : [B, H, N, D] contiguous, D innermost, dtype `dtype`.
  *   lse        : [B, H, N] float32.
@@ -176,7 +177,7 @@ int sattn_fwd_cache(int dtype, const void* q, const void* k, const void* v, void
  * normalized row with probabilities recomputed from the saved lse; lesson
  * 05: the query heads sharing a KV head add their gradients into it;
  * "Intermediate and advanced extension", softmax-backward row: the
- * vector-Jacobian product without a dense Jacobian).
+ * gradient is formed row by row from P and dP, never as an N x N Jacobian).
  *
  *   q, o, dout, dq : [B, Hq, N, D];  k, v, dk, dv : [B, Hkv, N, D]  (dtype).
  *   lse            : [B, Hq, N] float32, as written by sattn_fwd /
@@ -322,9 +323,9 @@ int sattn_fwd_sparse(int dtype, const void* q, const void* k, const void* v, voi
 /*
  * sattn_fwd_cache on strided, sliced, transposed or broadcast read-only
  * inputs, loaded in place ("Intermediate and advanced extension", workshop
- * table, strided-softmax row: address both strides and accept transposed,
- * sliced and broadcast read-only inputs; "Intermediate and advanced workshop
- * validation": direct loads against copy-then-kernel).
+ * table, strided-softmax row: inputs addressed through their row and
+ * element strides, so views need no copy; "Intermediate and advanced
+ * workshop validation": direct loads against copy-then-kernel).
  *
  *   q_strides  : host int64[3], element strides of q's batch, head and row
  *                dims (q[b, h, i, d] at q + b*s[0] + h*s[1] + i*s[2] + d).

@@ -20,16 +20,16 @@ with the HIP path:
 Sources (pages, by title and section):
   * "Intermediate and advanced extension", workshop table (online normalization
     row: mergeable (maximum, exponential sum) state with partition and
-    merge-order invariance; streaming attention row: tile QK and PV with online
-    rescaling, causal and noncausal) and "Logic review before implementation"
+    merge-order invariance; streaming attention row: the score and value
+    products tile by tile under a running rescale, causal or not) and "Logic review before implementation"
     (a state with no keys yet, whose maximum is -inf, is a special case of its
     own; the output sum is scaled together with the exponential sum; a causal
     row sees the key at its own position).
   * "Intermediate and advanced workshop validation", "Correctness and review"
     (dense FP64 references, future-value perturbation, large-logit cases,
     explicit empty+empty identity).
-  * "Attention algorithms and data movement", lessons 01 (merge normalized
-    attention without averaging tile outputs; a stated result for a row that sees no key),
+  * "Attention algorithms and data movement", lessons 01 (tile outputs are
+    combined through their rescaled sums, never averaged; a defined result for a row with no key),
     03 (saved normalization state), 04 (packed causal eligibility from logical
     positions), 05 (GQA query-head to KV-head mapping).
 

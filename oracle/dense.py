@@ -179,8 +179,8 @@ def split_partials(q, k, v, scale, chunk, causal=False, q_pos=None):
 
     Causal: key j is eligible for row i iff j <= q_pos[i] (q_pos defaults to
     ``cache_positions(Nq, Nk)``). A chunk with no eligible key for a row gives
-    that row the empty state m = -inf, l = 0, acc = 0 (lesson 01: the
-    explicit identity of the merge).
+    that row the empty state m = -inf, l = 0, acc = 0, the element that
+    leaves any other state unchanged when merged with it (lesson 01).
 
     q: [Nq, D], k, v: [Nk, D]. Returns m [Nq, C], l [Nq, C], acc [Nq, C, Dv].
     """

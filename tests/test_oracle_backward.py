@@ -2,8 +2,8 @@
 SDPA, central finite differences, grouped heads against summed expanded
 heads, and closed forms (constant values give zero dQ and dK; the rows of P
 sum to one, so the dV rows sum to the dO rows). The pages ask for exactly
-these references ("Intermediate and advanced workshop validation":
-backward against FP64 autograd and a central finite difference).
+these references ("Intermediate and advanced workshop validation",
+backward checks: float64 autograd and finite differences).
 """
 import math
 

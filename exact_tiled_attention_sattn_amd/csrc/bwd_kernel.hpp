@@ -212,7 +212,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdParams p) {
       }
     }
     delta = sum_halves(delta);
-    const float lse2 = row_ok ? p.lse[lbase + qrow] * kLog2e : 0.f;
+    // A row with no eligible key (lse = -inf) has every key masked to -inf
+    // below; a reference of +inf keeps its P at exp2(-inf) = 0, not NaN.
+    float lse2 = row_ok ? p.lse[lbase + qrow] * kLog2e : 0.f;
+    if (lse2 == -INFINITY) lse2 = INFINITY;
     if (row_ok && hf == 0) p.delta[lbase + qrow] = delta;
 
     f32x16 acc[DB];
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdParams p) {
       if (idx + 1 < nsteps) issue_tile(tile_of(idx + 1), nxt);
       const int kt0 = tile_of(idx) * BN;
       if (!wave_active || (CAUSAL && kt0 > wave_last_pos)) return;
-      bool edge = kt0 + BN > klen || (CAUSAL && kt0 + BN - 1 > q_pos0 + off + wave * 32);
+      bool edge = kt0 + BN > klen || (CAUSAL && kt0 + BN - 1 > q_pos0 + off + wave_u * 32);
       if constexpr (LAYOUT == BWD_SPARSE) {
         // the wave's 32 rows lie in one mask row block and the tile's keys in
         // one key block (block_q % 32 == 0, block_k % 64 == 0)
@@ -298,17 +301,41 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdParams p) {
           dp[kb] = E::mfma32(*(const u32x4*)(sV + kofs[kk] + kb * 32 * D), dreg[kk], dp[kb]);
         }
       }
-      // P = exp2(S c - lse log2 e) on eligible keys; dS = P (dP - Delta)
+      // Ineligible keys: S = -inf, so that P = exp2(-inf) = 0 below. Only
+      // tiles that straddle the diagonal, the key tail or a sparse block edge
+      // take this pass (a select on every element of every tile nearly
+      // doubled the tile's VALU work); the scale is > 0, so -inf stays -inf.
+      if (edge) {
+        if constexpr (LAYOUT == BWD_SPARSE) {
+          // the eligibility rule of sparse_pair, as straight-line selects
+          const int wlo = p.win_left < 0 ? INT_MIN : my_pos - p.win_left;
+          const int whi = p.win_right < 0 ? INT_MAX : my_pos + p.win_right;
+          const int hi = CAUSAL ? min(klen - 1, my_pos) : klen - 1;
+          const bool grow = my_pos < p.n_global;
+  #pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+              const bool ok = (key <= hi) & (((key >= wlo) & (key <= whi)) | (key < p.n_global) | grow);
+              s[kb][r] = ok ? s[kb][r] : -INFINITY;
+            }
+        } else {
+          // the last eligible key, as an offset from this lane's first key of the tile
+          const int lim = (CAUSAL ? min(klen - 1, my_pos) : klen - 1) - (kt0 + 4 * hf);
+  #pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+        }
+      }
+      // P = exp2(S c - lse log2 e); dS = P (dP - Delta)
   #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
   #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(fmaf(s[kb][r], p.c, -lse2));
-          if (edge) {
-            const int key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= klen || (CAUSAL && key > my_pos) || (LAYOUT == BWD_SPARSE && !sparse_pair(p, my_pos, key)))
-              pr = 0.f;
-          }
+          const float pr = fast_exp2(fmaf(s[kb][r], p.c, -lse2));
           s[kb][r] = pr * (dp[kb][r] - delta);
         }
       // dQ^T += K^T dS^T (16 keys per MFMA; K^T by transposing reads)

@@ -44,6 +44,7 @@ struct BwdParams {
                         // (Nk - Nq: queries are the last Nq tokens; 0 for equal lengths)
   int nqt;              // dQ kernel: query tiles per head (varlen: per longest sequence)
   int pair;             // dQ kernel, batched causal: workgroup j takes query tiles nqt-1-j and j
+  int pair_kv;          // dK/dV in two roles, batched causal: workgroup j takes key tiles j and nkt-1-j
   int nkt;              // dK/dV kernel: 128-key tiles per KV head (varlen: per longest sequence)
   // varlen: q, o, dout, dq are [T, Hq, D] and k, v, dk, dv [T, Hkv, D]
   // packed tokens, lse and Delta [Hq, T]; sequence s owns tokens
@@ -396,14 +397,16 @@ struct KvWalk {
   int nkeys;                   // keys of this workgroup
   int t_begin, per_head, npre, band0, nsteps;
 
-  // false if the workgroup has no keys (uniform over the workgroup)
-  __device__ __forceinline__ bool init(const BwdParams& p) {
+  // false if the workgroup has no keys for this item (uniform over the
+  // workgroup); item 1 exists only for paired batched causal grids
+  __device__ __forceinline__ bool init(const BwdParams& p, int item = 0) {
     grp = p.hq / p.hkv;
     off = 0;
     tok0 = 0;
     bq = 0;
     const int lin = xcd_linear(blockIdx.x);
     if constexpr (VARLEN) {
+      if (item > 0) return false;
       const int per_g = p.nseq * p.nkt;
       g = lin / per_g;
       const int sq = (lin % per_g) / p.nkt;
@@ -420,8 +423,19 @@ struct KvWalk {
       kv_rs = (int64_t)p.hkv * D;
       kvbase = (int64_t)(a + k0) * kv_rs + (int64_t)g * D;
     } else {
-      const int kvs = lin / p.nkt;   // b * Hkv + g
-      const int kt = lin % p.nkt;
+      int kvs, kt;   // kvs = b * Hkv + g
+      if (CAUSAL && p.pair_kv) {
+        // the longer key tile j (its keys see the most queries), then nkt-1-j
+        const int npairs = (p.nkt + 1) / 2;
+        kvs = lin / npairs;
+        const int j = lin % npairs;
+        kt = item == 0 ? j : p.nkt - 1 - j;
+        if (item == 1 && kt == j) return false;   // odd count: the middle tile once
+      } else {
+        if (item > 0) return false;
+        kvs = lin / p.nkt;
+        kt = lin % p.nkt;
+      }
       bq = kvs / p.hkv;
       g = kvs % p.hkv;
       len = p.nk;
@@ -753,220 +767,227 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_roles_kernel(const BwdParams 
   // P of the current step: [key block][32-query block][register group][lane]
   __shared__ __attribute__((aligned(16))) f32x4 pex[4][2][4][64];
 
-  KvWalk<D, CAUSAL, LAYOUT> wk;
-  if (!wk.init(p)) return;   // uniform over the workgroup
-  const int len = wk.len, qlen = wk.qlen, off = wk.off, k0 = wk.k0;
-  const int64_t kvbase = wk.kvbase, kv_rs = wk.kv_rs;
-  const int nkeys = wk.nkeys;
+  // Batched causal grids at D = 128 pair key tiles (j, nkt-1-j), so that
+  // every workgroup walks about the same number of query steps.
+  constexpr int NITEMS = (LAYOUT == BWD_DENSE && CAUSAL && D == 128) ? 2 : 1;
+#pragma unroll 1
+  for (int item = 0; item < NITEMS; ++item) {
+    if (item > 0) __syncthreads();   // the previous item's stores have left the tile buffers
+    KvWalk<D, CAUSAL, LAYOUT> wk;
+    if (!wk.init(p, item)) continue;   // uniform over the workgroup
+    const int len = wk.len, qlen = wk.qlen, off = wk.off, k0 = wk.k0;
+    const int64_t kvbase = wk.kvbase, kv_rs = wk.kv_rs;
+    const int nkeys = wk.nkeys;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int l32 = lane & 31, hf = lane >> 5;
-  const bool role_p = wave_u < 4;
-  const int kw = wave_u & 3;                    // the pair's 32-key block
-  const int krow = kw * 32 + l32;
-  const bool key_ok = krow < nkeys;
-  const int my_key = k0 + krow;
-  const bool wave_active = kw * 32 < nkeys;
-  const int wave_first_key = k0 + kw * 32;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const bool role_p = wave_u < 4;
+    const int kw = wave_u & 3;                    // the pair's 32-key block
+    const int krow = kw * 32 + l32;
+    const bool key_ok = krow < nkeys;
+    const int my_key = k0 + krow;
+    const bool wave_active = kw * 32 < nkeys;
+    const int wave_first_key = k0 + kw * 32;
 
-  const int nsteps = wk.nsteps;
-  TileLoader<D, NW> ld;
-  ld.init(wave, lane, wk.row_bytes());
-  auto issue_step = [&](int it, uint16_t* sb) { wk.issue(p, ld, it, sb, wave_u, lane); };
+    const int nsteps = wk.nsteps;
+    TileLoader<D, NW> ld;
+    ld.init(wave, lane, wk.row_bytes());
+    auto issue_step = [&](int it, uint16_t* sb) { wk.issue(p, ld, it, sb, wave_u, lane); };
 
-  int aofs[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) aofs[kk] = l32 * D + (((kk * 2 + hf) ^ swz<D>(l32)) * 8);
-  const int g16 = lane >> 4;
-  const int tr_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
-  int tofs[2][DB];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d0 = db * 32 + 16 * (g16 & 1) + 4 * (lane & 3);
-      const int row = tr_row + 8 * x;
-      tofs[x][db] = row * D + (((d0 >> 3) ^ swz<D>(row)) * 8) + (d0 & 7);
-    }
-
-
-  // Which 32-query blocks of a step a pair computes, and which need the
-  // element mask (queries past the end; causal: a query before a key of the
-  // pair; sparse: a pair the rule drops). Both roles take the same decisions.
-  const int wkey1 = min(wave_first_key + 31, len - 1);
-  auto blk_need = [&](int hh, int qb0) {
-    if (CAUSAL && qb0 + off + 31 < wave_first_key) return false;   // every query precedes the keys
-    if constexpr (SPARSE)
-      return qb0 < qlen && sparse_bit(p, hh, qb0, wave_first_key) &&
-             sparse_any(p, qb0, min(qb0 + 31, qlen - 1), wave_first_key, wkey1);
-    return true;
-  };
-  auto blk_edge = [&](int qb0) {
-    return qb0 + 32 > qlen || (CAUSAL && qb0 + off < wave_first_key + 31) ||
-           (SPARSE && !sparse_all(p, qb0, min(qb0 + 31, qlen - 1), wave_first_key, wkey1));
-  };
-  // A operand of S = Q K^T / dP = dO V^T: 32 rows of the tile, k-steps of 16 d
-  auto rows_mfma = [&](const uint16_t* sT, int qb, const u32x4 (&breg)[KK], f32x16& acc) {
-    u32x4 a[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) a[kk] = *(const u32x4*)(sT + aofs[kk] + qb * 32 * D);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) acc = E::mfma32(a[kk], breg[kk], acc);
-  };
-  // acc^T += T^T X for one 32-query block: T^T from transposing reads of the
-  // tile, X the packed block (16 queries per MFMA)
-  auto tr_mfma = [&](const uint16_t* sT, int qb, const u32x4 (&x)[2], f32x16 (&acc)[DB]) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int qrow = (qb * 32 + half * 16) * D;
-#pragma unroll
+    int aofs[KK];
+  #pragma unroll
+    for (int kk = 0; kk < KK; ++kk) aofs[kk] = l32 * D + (((kk * 2 + hf) ^ swz<D>(l32)) * 8);
+    const int g16 = lane >> 4;
+    const int tr_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
+    int tofs[2][DB];
+  #pragma unroll
+    for (int x = 0; x < 2; ++x)
+  #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x2 a0 = lds_read_tr16(sT + tofs[0][db] + qrow);
-        const u32x2 a1 = lds_read_tr16(sT + tofs[1][db] + qrow);
-        acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, x[half], acc[db]);
+        const int d0 = db * 32 + 16 * (g16 & 1) + 4 * (lane & 3);
+        const int row = tr_row + 8 * x;
+        tofs[x][db] = row * D + (((d0 >> 3) ^ swz<D>(row)) * 8) + (d0 & 7);
       }
-    }
-  };
-  auto pack16 = [&](const f32x16& v, u32x4 (&x)[2]) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int o8 = half * 8;
-      x[half] = u32x4{E::pack2(v[o8 + 0], v[o8 + 1]), E::pack2(v[o8 + 2], v[o8 + 3]),
-                      E::pack2(v[o8 + 4], v[o8 + 5]), E::pack2(v[o8 + 6], v[o8 + 7])};
-    }
-  };
 
-  f32x16 acc[DB];   // dV (P role) or dK (dS role), transposed: [d][key]
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  if (nsteps > 0) issue_step(0, sbuf0);
 
-  if (role_p) {
-    // ---- P role: K as the B operand of S = Q K^T
-    u32x4 kreg[KK];
-    {
-      const int64_t o_ = kvbase + (int64_t)krow * kv_rs + hf * 8;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kreg[kk] = key_ok ? *(const u32x4*)(p.k + o_ + kk * 16) : u32x4{0, 0, 0, 0};
-    }
-    auto step = [&](int it, const uint16_t* cur, uint16_t* nxt) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();   // tile it visible; every wave is done with tile it-1 and the previous P
-      if (it + 1 < nsteps) issue_step(it + 1, nxt);
-      const int q0 = wk.q0(it);
-      const int hh = wk.head(it);
-      const uint16_t* sQ = cur;
-      const uint16_t* sD = cur + TILE;
-      const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
-      u32x4 pb[2][2];
-      // P = exp2(S c - lse log2 e) of block qb in place, masked on edge
-      // blocks, and to LDS for the partner
-      auto probs = [&](int qb, int qb0, f32x16& s, auto edge_tag) {
-        constexpr bool EDGE = decltype(edge_tag)::value;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 l4 = *(const f32x4*)(sL + qb * 32 + 8 * g4 + 4 * hf);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = g4 * 4 + i;
-            float x = fast_exp2(fmaf(s[r], p.c, -l4[i] * kLog2e));
-            if constexpr (EDGE) {
-              const int qi = qb0 + 8 * g4 + 4 * hf + i;
-              if (qi >= qlen || (CAUSAL && my_key > qi + off) || (SPARSE && !sparse_pair(p, qi, my_key))) x = 0.f;
+    // Which 32-query blocks of a step a pair computes, and which need the
+    // element mask (queries past the end; causal: a query before a key of the
+    // pair; sparse: a pair the rule drops). Both roles take the same decisions.
+    const int wkey1 = min(wave_first_key + 31, len - 1);
+    auto blk_need = [&](int hh, int qb0) {
+      if (CAUSAL && qb0 + off + 31 < wave_first_key) return false;   // every query precedes the keys
+      if constexpr (SPARSE)
+        return qb0 < qlen && sparse_bit(p, hh, qb0, wave_first_key) &&
+               sparse_any(p, qb0, min(qb0 + 31, qlen - 1), wave_first_key, wkey1);
+      return true;
+    };
+    auto blk_edge = [&](int qb0) {
+      return qb0 + 32 > qlen || (CAUSAL && qb0 + off < wave_first_key + 31) ||
+             (SPARSE && !sparse_all(p, qb0, min(qb0 + 31, qlen - 1), wave_first_key, wkey1));
+    };
+    // A operand of S = Q K^T / dP = dO V^T: 32 rows of the tile, k-steps of 16 d
+    auto rows_mfma = [&](const uint16_t* sT, int qb, const u32x4 (&breg)[KK], f32x16& acc) {
+      u32x4 a[KK];
+  #pragma unroll
+      for (int kk = 0; kk < KK; ++kk) a[kk] = *(const u32x4*)(sT + aofs[kk] + qb * 32 * D);
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  #pragma unroll
+      for (int kk = 0; kk < KK; ++kk) acc = E::mfma32(a[kk], breg[kk], acc);
+    };
+    // acc^T += T^T X for one 32-query block: T^T from transposing reads of the
+    // tile, X the packed block (16 queries per MFMA)
+    auto tr_mfma = [&](const uint16_t* sT, int qb, const u32x4 (&x)[2], f32x16 (&acc)[DB]) {
+  #pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int qrow = (qb * 32 + half * 16) * D;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x2 a0 = lds_read_tr16(sT + tofs[0][db] + qrow);
+          const u32x2 a1 = lds_read_tr16(sT + tofs[1][db] + qrow);
+          acc[db] = E::mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, x[half], acc[db]);
+        }
+      }
+    };
+    auto pack16 = [&](const f32x16& v, u32x4 (&x)[2]) {
+  #pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int o8 = half * 8;
+        x[half] = u32x4{E::pack2(v[o8 + 0], v[o8 + 1]), E::pack2(v[o8 + 2], v[o8 + 3]),
+                        E::pack2(v[o8 + 4], v[o8 + 5]), E::pack2(v[o8 + 6], v[o8 + 7])};
+      }
+    };
+
+    f32x16 acc[DB];   // dV (P role) or dK (dS role), transposed: [d][key]
+  #pragma unroll
+    for (int db = 0; db < DB; ++db)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    if (nsteps > 0) issue_step(0, sbuf0);
+
+    if (role_p) {
+      // ---- P role: K as the B operand of S = Q K^T
+      u32x4 kreg[KK];
+      {
+        const int64_t o_ = kvbase + (int64_t)krow * kv_rs + hf * 8;
+  #pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kreg[kk] = key_ok ? *(const u32x4*)(p.k + o_ + kk * 16) : u32x4{0, 0, 0, 0};
+      }
+      auto step = [&](int it, const uint16_t* cur, uint16_t* nxt) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();   // tile it visible; every wave is done with tile it-1 and the previous P
+        if (it + 1 < nsteps) issue_step(it + 1, nxt);
+        const int q0 = wk.q0(it);
+        const int hh = wk.head(it);
+        const uint16_t* sQ = cur;
+        const uint16_t* sD = cur + TILE;
+        const float* sL = reinterpret_cast<const float*>(cur + 2 * TILE);
+        u32x4 pb[2][2];
+        // P = exp2(S c - lse log2 e) of block qb in place, masked on edge
+        // blocks, and to LDS for the partner
+        auto probs = [&](int qb, int qb0, f32x16& s, auto edge_tag) {
+          constexpr bool EDGE = decltype(edge_tag)::value;
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 l4 = *(const f32x4*)(sL + qb * 32 + 8 * g4 + 4 * hf);
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = g4 * 4 + i;
+              float x = fast_exp2(fmaf(s[r], p.c, -l4[i] * kLog2e));
+              if constexpr (EDGE) {
+                const int qi = qb0 + 8 * g4 + 4 * hf + i;
+                if (qi >= qlen || (CAUSAL && my_key > qi + off) || (SPARSE && !sparse_pair(p, qi, my_key))) x = 0.f;
+              }
+              s[r] = x;
             }
-            s[r] = x;
+            pex[kw][qb][g4][lane] = f32x4{s[g4 * 4 + 0], s[g4 * 4 + 1], s[g4 * 4 + 2], s[g4 * 4 + 3]};
           }
-          pex[kw][qb][g4][lane] = f32x4{s[g4 * 4 + 0], s[g4 * 4 + 1], s[g4 * 4 + 2], s[g4 * 4 + 3]};
+        };
+        if (wave_active) {
+  #pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const int qb0 = q0 + qb * 32;
+            if (!blk_need(hh, qb0)) continue;
+            f32x16 s;
+            rows_mfma(sQ, qb, kreg, s);
+            if (blk_edge(qb0)) probs(qb, qb0, s, std::true_type{});
+            else probs(qb, qb0, s, std::false_type{});
+            pack16(s, pb[qb]);
+          }
+        }
+        __syncthreads();   // P of both blocks in LDS
+        if (wave_active) {
+  #pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            if (blk_need(hh, q0 + qb * 32)) tr_mfma(sD, qb, pb[qb], acc);   // dV^T += dO^T P
         }
       };
-      if (wave_active) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int qb0 = q0 + qb * 32;
-          if (!blk_need(hh, qb0)) continue;
-          f32x16 s;
-          rows_mfma(sQ, qb, kreg, s);
-          if (blk_edge(qb0)) probs(qb, qb0, s, std::true_type{});
-          else probs(qb, qb0, s, std::false_type{});
-          pack16(s, pb[qb]);
+      int it = 0;
+      for (; it + 1 < nsteps; it += 2) {
+        step(it, sbuf0, sbuf1);
+        step(it + 1, sbuf1, sbuf0);
+      }
+      if (it < nsteps) step(it, sbuf0, sbuf1);
+      __syncthreads();   // every wave is done with the tile buffers, which stage the stores
+      store_tile_rows<E, D>(acc, 1.0f, sbuf0 + kw * 32 * D, p.dv + kvbase + (int64_t)kw * 32 * kv_rs, kv_rs,
+                            nkeys - kw * 32);
+    } else {
+      // ---- dS role: V as the B operand of dP = dO V^T
+      u32x4 vreg[KK];
+      {
+        const int64_t o_ = kvbase + (int64_t)krow * kv_rs + hf * 8;
+  #pragma unroll
+        for (int kk = 0; kk < KK; ++kk) vreg[kk] = key_ok ? *(const u32x4*)(p.v + o_ + kk * 16) : u32x4{0, 0, 0, 0};
+      }
+      auto step = [&](int it, const uint16_t* cur, uint16_t* nxt) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (it + 1 < nsteps) issue_step(it + 1, nxt);
+        const int q0 = wk.q0(it);
+        const int hh = wk.head(it);
+        const uint16_t* sQ = cur;
+        const uint16_t* sD = cur + TILE;
+        const float* sE = reinterpret_cast<const float*>(cur + 2 * TILE) + BMQ;
+        f32x16 dp[2];
+        if (wave_active) {
+  #pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            if (blk_need(hh, q0 + qb * 32)) rows_mfma(sD, qb, vreg, dp[qb]);
         }
+        __syncthreads();   // the partner's P of both blocks in LDS
+        // dS = P (dP - Delta) of block qb, packed
+        auto dscores = [&](int qb, u32x4 (&sb)[2]) {
+          f32x16 ds;
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 pr = pex[kw][qb][g4][lane];
+            const f32x4 d4 = *(const f32x4*)(sE + qb * 32 + 8 * g4 + 4 * hf);
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) ds[g4 * 4 + i] = pr[i] * (dp[qb][g4 * 4 + i] - d4[i]);
+          }
+          pack16(ds, sb);
+        };
+        if (wave_active) {
+  #pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            if (!blk_need(hh, q0 + qb * 32)) continue;
+            u32x4 sb[2];
+            dscores(qb, sb);
+            tr_mfma(sQ, qb, sb, acc);   // dK^T += Q^T dS
+          }
+        }
+      };
+      int it = 0;
+      for (; it + 1 < nsteps; it += 2) {
+        step(it, sbuf0, sbuf1);
+        step(it + 1, sbuf1, sbuf0);
       }
-      __syncthreads();   // P of both blocks in LDS
-      if (wave_active) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          if (blk_need(hh, q0 + qb * 32)) tr_mfma(sD, qb, pb[qb], acc);   // dV^T += dO^T P
-      }
-    };
-    int it = 0;
-    for (; it + 1 < nsteps; it += 2) {
-      step(it, sbuf0, sbuf1);
-      step(it + 1, sbuf1, sbuf0);
-    }
-    if (it < nsteps) step(it, sbuf0, sbuf1);
-    __syncthreads();   // every wave is done with the tile buffers, which stage the stores
-    store_tile_rows<E, D>(acc, 1.0f, sbuf0 + kw * 32 * D, p.dv + kvbase + (int64_t)kw * 32 * kv_rs, kv_rs,
-                          nkeys - kw * 32);
-  } else {
-    // ---- dS role: V as the B operand of dP = dO V^T
-    u32x4 vreg[KK];
-    {
-      const int64_t o_ = kvbase + (int64_t)krow * kv_rs + hf * 8;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) vreg[kk] = key_ok ? *(const u32x4*)(p.v + o_ + kk * 16) : u32x4{0, 0, 0, 0};
-    }
-    auto step = [&](int it, const uint16_t* cur, uint16_t* nxt) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (it < nsteps) step(it, sbuf0, sbuf1);
       __syncthreads();
-      if (it + 1 < nsteps) issue_step(it + 1, nxt);
-      const int q0 = wk.q0(it);
-      const int hh = wk.head(it);
-      const uint16_t* sQ = cur;
-      const uint16_t* sD = cur + TILE;
-      const float* sE = reinterpret_cast<const float*>(cur + 2 * TILE) + BMQ;
-      f32x16 dp[2];
-      if (wave_active) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          if (blk_need(hh, q0 + qb * 32)) rows_mfma(sD, qb, vreg, dp[qb]);
-      }
-      __syncthreads();   // the partner's P of both blocks in LDS
-      // dS = P (dP - Delta) of block qb, packed
-      auto dscores = [&](int qb, u32x4 (&sb)[2]) {
-        f32x16 ds;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 pr = pex[kw][qb][g4][lane];
-          const f32x4 d4 = *(const f32x4*)(sE + qb * 32 + 8 * g4 + 4 * hf);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ds[g4 * 4 + i] = pr[i] * (dp[qb][g4 * 4 + i] - d4[i]);
-        }
-        pack16(ds, sb);
-      };
-      if (wave_active) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (!blk_need(hh, q0 + qb * 32)) continue;
-          u32x4 sb[2];
-          dscores(qb, sb);
-          tr_mfma(sQ, qb, sb, acc);   // dK^T += Q^T dS
-        }
-      }
-    };
-    int it = 0;
-    for (; it + 1 < nsteps; it += 2) {
-      step(it, sbuf0, sbuf1);
-      step(it + 1, sbuf1, sbuf0);
+      store_tile_rows<E, D>(acc, p.scale, sbuf1 + kw * 32 * D, p.dk + kvbase + (int64_t)kw * 32 * kv_rs, kv_rs,
+                            nkeys - kw * 32);
     }
-    if (it < nsteps) step(it, sbuf0, sbuf1);
-    __syncthreads();
-    store_tile_rows<E, D>(acc, p.scale, sbuf1 + kw * 32 * D, p.dk + kvbase + (int64_t)kw * 32 * kv_rs, kv_rs,
-                          nkeys - kw * 32);
   }
 }
 

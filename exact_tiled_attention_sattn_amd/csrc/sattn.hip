@@ -520,7 +520,12 @@ static int bwd_impl(int dtype, const void* q, const void* k, const void* v, cons
   // dQ: BM = bmq rows per workgroup; batched causal grids of at least 1024
   // query tiles pair them (tiles nqt-1-j and j per workgroup)
   p.pair = (!sp && causal && bmq == 256 && B * Hq * p.nqt >= 1024) ? 1 : 0;
-  const int64_t grid_q = B * Hq * (p.pair ? (p.nqt + 1) / 2 : p.nqt), grid_kv = B * Hkv * p.nkt;
+  // dK/dV at D = 128 (two roles, one workgroup per CU): batched causal grids
+  // of at least 1024 key tiles pair them too (tiles j and nkt-1-j per
+  // workgroup). At D = 64 two workgroups share a CU and pairing was slower.
+  p.pair_kv = (!sp && causal && D == 128 && B * Hkv * p.nkt >= 1024) ? 1 : 0;
+  const int64_t grid_q = B * Hq * (p.pair ? (p.nqt + 1) / 2 : p.nqt);
+  const int64_t grid_kv = B * Hkv * (p.pair_kv ? (p.nkt + 1) / 2 : p.nkt);
   if (grid_q >= (int64_t(1) << 31)) return fail(SATTN_ERR_UNSUPPORTED, "grid too large");
   if (sp) {
     p.win_left = (int)sp->left;

@@ -1216,12 +1216,42 @@ def test_backward_batched_4x16x4096x128_bf16_two_heads():
         _check_grads((dq[sl], dk[sl], dv[sl]), tuple(r[None, None] for r in refs), q[sl], k[sl], v[sl], do[sl],
                      o[sl], scale, True, torch.bfloat16, "[%d,%d] " % (bi, hi))
         # This grid pairs its dQ query tiles (tiles nqt-1-j and j per
-        # workgroup); one slice alone runs unpaired. The gradients of the
-        # slice do not depend on which tiles share a workgroup.
+        # workgroup) and its dK/dV key tiles (j and nkt-1-j); one slice alone
+        # runs unpaired. The gradients of the slice do not depend on which
+        # tiles share a workgroup.
         one = sattn_bwd(*(x[sl].contiguous() for x in (qd, kd, vd, o, dod)), lse[sl].contiguous(), causal=True,
                         scale=scale)
         for a, b_, name in zip((dq[sl], dk[sl], dv[sl]), one, ("dq", "dk", "dv")):
             assert torch.equal(a, b_), "[%d,%d] %s of the batched call differs from the slice alone" % (bi, hi, name)
+
+
+def test_backward_paired_grids_odd_tile_counts():
+    """Causal D = 128, N = 4200 (ragged): 17 dQ query tiles of 256 and 33
+    dK/dV key tiles of 128 per head, 64 heads, so both grids pair their
+    tiles and take the middle tile once. One head against the float64
+    gradients, two heads bit for bit against the same slices run alone
+    (unpaired)."""
+    _banner("backward paired grids, odd tile counts")
+    from oracle import backward
+    b, h, n, d = 1, 64, 4200, 128
+    q, k, v = W.qkv((b, h, n, d), (b, h, n, d), "bf16", 41)
+    do = W.randn((b, h, n, d), "bf16", torch.Generator().manual_seed(42))
+    scale = W.scale_f32(d)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = sattn_fwd(qd, kd, vd, causal=True, scale=scale)
+    dq, dk, dv = sattn_bwd(qd, kd, vd, o, dod, lse, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    sl = (slice(0, 1), slice(63, 64))
+    refs = backward.attention_backward(W.to_f64(q[0, 63]), W.to_f64(k[0, 63]), W.to_f64(v[0, 63]),
+                                       W.to_f64(do[0, 63]), scale, True)
+    _check_grads((dq[sl], dk[sl], dv[sl]), tuple(r[None, None] for r in refs), q[sl], k[sl], v[sl], do[sl],
+                 o[sl], scale, True, torch.bfloat16, "[0,63] ")
+    for hi in (0, 63):
+        sl = (slice(0, 1), slice(hi, hi + 1))
+        one = sattn_bwd(*(x[sl].contiguous() for x in (qd, kd, vd, o, dod)), lse[sl].contiguous(), causal=True,
+                        scale=scale)
+        for a, b_, name in zip((dq[sl], dk[sl], dv[sl]), one, ("dq", "dk", "dv")):
+            assert torch.equal(a, b_), "[0,%d] %s of the paired call differs from the slice alone" % (hi, name)
 
 
 @pytest.mark.parametrize("growth", [3.0, 50.0])

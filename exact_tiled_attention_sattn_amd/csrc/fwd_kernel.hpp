@@ -469,7 +469,7 @@ __device__ __forceinline__ void attn_rows(const FwdParams& p, const Work& w, uin
   // Sparse mode walks a list of the key tiles some wave needs (built below):
   // entry = tile | (waves that need it) << 16 | (element mask needed) << 24.
   int nact = 0;
-  auto body = [&](int idx, int t, int e, const uint16_t* cur, auto mask_tag, auto fast_tag) {
+  auto body = [&](int /* list index */, int t, int e, const uint16_t* cur, auto mask_tag, auto fast_tag) {
     constexpr bool MASKED = decltype(mask_tag)::value;
     constexpr bool FAST = decltype(fast_tag)::value;
     const int kt0 = w.k_begin + t * BN;

@@ -35,7 +35,7 @@ constexpr int kCacheWideRows = 512;
 // Waves of the backward dQ kernel: 8 (256 queries per workgroup) for the
 // batched layout at D = 128 (causal grids of enough tiles then pair their
 // query tiles, as the forward does), else 4.
-constexpr int bwd_dq_waves(int D, bool causal, int layout) {
+constexpr int bwd_dq_waves(int D, bool /* causal: the same either way */, int layout) {
   return (D == 128 && layout == BWD_DENSE) ? 8 : 4;
 }
 

@@ -539,6 +539,53 @@ def prefill_extra():
             "frac_of_bf16_peak": flops / tm["graph_us"]["median"] / 1e6 / PEAK_BF16_TFLOPS}
 
 
+def gqa_token_decode_extra():
+    """Single-token decode with grouped KV heads: 1 query per head against a
+    32768-token K/V cache, B=16, 32 query heads on 8 KV heads, D=128 bf16,
+    chunks of 2048 (split partials, then the merge). Bytes count K/V once."""
+    import torch
+    from exact_tiled_attention_sattn_amd import sattn_fwd_split, sattn_merge
+    b, hq, hkv, nq, nk, d, chunk = 16, 32, 8, 1, 32768, 128, 2048
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    q = W.randn_device_sliced((b, hq, nq, d), "bf16", g, DEV)
+    k = W.randn_device_sliced((b, hkv, nk, d), "bf16", g, DEV)
+    v = W.randn_device_sliced((b, hkv, nk, d), "bf16", g, DEV)
+    c = -(-nk // chunk)
+    pm = torch.empty((b, hq, nq, c), dtype=torch.float32, device=DEV)
+    pl = torch.empty_like(pm)
+    pa = torch.empty((b, hq, nq, c, d), dtype=torch.float32, device=DEV)
+    o = torch.empty((b, hq, nq, d), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((b, hq, nq), dtype=torch.float32, device=DEV)
+    scale = W.scale_f32(d)
+    split = lambda: sattn_fwd_split(q, k, v, chunk, scale, part_m=pm, part_l=pl, part_acc=pa)  # noqa: E731
+    merge = lambda: sattn_merge(pm, pl, pa, torch.bfloat16, out=o, lse=lse)  # noqa: E731
+
+    def both():
+        split()
+        merge()
+    both()
+    torch.cuda.synchronize()
+    rows = torch.arange(nq)
+    grp = hq // hkv
+    gate = worst(gate_rows(o[bb, h].cpu(), lse[bb, h].cpu(), q[bb, h], k[bb, h // grp], v[bb, h // grp], scale,
+                           False, rows, rows + nk - nq, torch.bfloat16, "gate gqa token decode")
+                 for bb, h in ((0, 0), (6, 13), (15, 31)))
+    replay_ok = replay_matches(both, [o, lse])
+    t = time_variants({"split+merge": both, "split": split, "merge": merge}, seed=9)
+    kv_bytes = 2 * b * hkv * nk * d * 2
+    part_bytes = b * hq * nq * c * (d + 2) * 4
+    split_bytes = kv_bytes + b * hq * nq * d * 2 + part_bytes
+    del q, k, v
+    torch.cuda.empty_cache()
+    return {"workload": "GQA single-token decode: 1 query per head vs 32768-token cache, B=16, 32q/8kv heads, "
+                        "D=128 bf16, chunk 2048",
+            "gate": gate, "graph_replay_bitwise": replay_ok, "timing": t, "algorithmic_bytes_split": split_bytes,
+            "split_GBps_graph": split_bytes / t["split"]["graph_us"]["median"] / 1e3,
+            "split_frac_of_hbm_peak": split_bytes / t["split"]["graph_us"]["median"] / 1e3 / PEAK_HBM_GBS,
+            "merge_us_graph": t["merge"]["graph_us"]["median"]}
+
+
 def gqa_decode_extra():
     """Causal decode of 4 new tokens per sequence against a 32768-token K/V
     cache: B=8, 32 query heads on 8 KV heads, D=128 bf16, chunks of 2048
@@ -1191,6 +1238,8 @@ def _counter_per_kernel(d, counter):
 EXTRA_TRAFFIC = [
     ("split-KV decode partials 16x32x131072x128 bf16", "split_row_kernel<Bf16, 128, false>",
      ("splitkv_decode", "algorithmic_bytes_split")),
+    ("GQA single-token decode partials, 1 q vs 32768 cached, B=16, 32q/8kv", "fwd_kernel<Bf16, 128, 64, 4, false, 2>",
+     ("gqa_token_decode", "algorithmic_bytes_split")),
     ("causal GQA decode partials, 4 q vs 32768 cached, B=8, 32q/8kv", "fwd_kernel<Bf16, 128, 64, 4, true, 2>",
      ("cache_gqa_decode", "algorithmic_bytes_split")),
 ]
@@ -1472,6 +1521,8 @@ def main():
         extras["cache_prefill"] = prefill_extra()
         log("causal GQA decode against a K/V cache")
         extras["cache_gqa_decode"] = gqa_decode_extra()
+        log("GQA single-token decode")
+        extras["gqa_token_decode"] = gqa_token_decode_extra()
         log("strided (transposed) inputs")
         extras["strided_transposed"] = strided_extra()
         log("sparse: window + globals, block mask")

@@ -212,6 +212,11 @@ SPLIT_SMALL = [
     (1, 1, 1, 1, 5, 128, 4096, "fp16"),
     (1, 2, 2, 1, 300, 128, 1, "bf16"),
     (1, 2, 2, 1, 4099, 128, 1030, "fp16"),
+    # one query row per head, 2, 4 or 8 query heads per KV head: the group's
+    # rows packed into one slice
+    (1, 8, 2, 1, 999, 64, 200, "fp16"),
+    (2, 4, 2, 1, 333, 32, 64, "bf16"),
+    (1, 8, 1, 1, 500, 128, 128, "bf16"),
 ]
 
 
@@ -237,12 +242,13 @@ def test_split_partials_and_merge_small(b, hq, hkv, nq, nk, d, chunk, dt):
             check_attention(o[bb, h], lse[bb, h], o_ref, lse_ref, W.DTYPES[dt], "merged")
 
 
-@pytest.mark.parametrize("d,dt", [(128, "bf16"), (64, "fp16")])
-def test_split_row_large_logits(d, dt):
-    """One query row per slice with Q x 16 (score spread of about 16 nats):
-    the row kernel's running maximum changes many times within a chunk."""
-    _banner("split row large logits", d, dt)
-    q, k, v = W.qkv((2, 2, 1, d), (2, 2, 3000, d), dt, seed=2600 + d)
+@pytest.mark.parametrize("d,dt,hq,hkv", [(128, "bf16", 2, 2), (64, "fp16", 2, 2), (128, "bf16", 8, 2)])
+def test_split_row_large_logits(d, dt, hq, hkv):
+    """One query row per head with Q x 16 (score spread of about 16 nats):
+    the running maximum changes many times within a chunk, for a query head
+    alone (the row kernel) and for four sharing a KV head (packed)."""
+    _banner("split row large logits", d, dt, hq, hkv)
+    q, k, v = W.qkv((2, hq, 1, d), (2, hkv, 3000, d), dt, seed=2600 + d + hq)
     q = q * 16
     scale = W.scale_f32(d)
     chunk = 512
@@ -251,13 +257,14 @@ def test_split_row_large_logits(d, dt):
     torch.cuda.synchronize()
     qf, kf, vf = W.to_f64(q), W.to_f64(k), W.to_f64(v)
     pm_, pl_, pa_ = (x.cpu().double().numpy() for x in (pm, pl, pa))
+    g = hq // hkv
     for bb in range(2):
-        for h in range(2):
-            m_ref, l_ref, a_ref = dense.split_partials(qf[bb, h], kf[bb, h], vf[bb, h], scale, chunk)
+        for h in range(hq):
+            m_ref, l_ref, a_ref = dense.split_partials(qf[bb, h], kf[bb, h // g], vf[bb, h // g], scale, chunk)
             np.testing.assert_allclose(pm_[bb, h], m_ref, rtol=0, atol=1e-3 * max(1.0, np.abs(m_ref).max()))
             check_lse(pm_[bb, h] + np.log(pl_[bb, h]), m_ref + np.log(l_ref), "partial lse")
             check_o(pa_[bb, h] / pl_[bb, h][..., None], a_ref / l_ref[..., None], W.DTYPES[dt], "partial o")
-            o_ref, lse_ref = dense.attention(qf[bb, h], kf[bb, h], vf[bb, h], scale)
+            o_ref, lse_ref = dense.attention(qf[bb, h], kf[bb, h // g], vf[bb, h // g], scale)
             check_attention(o[bb, h], lse[bb, h], o_ref, lse_ref, W.DTYPES[dt], "merged")
 
 

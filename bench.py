@@ -32,6 +32,9 @@ Other modes:
                     two bench runs (their logs: --bench-log twice, in that
                     order) and writes the traffic summary
                     profiles/fwd_kernel_batched_4x16x4096x128_bf16_pmc.{md,json}.
+  --read-ceiling    times a bare streaming read of an 8 GiB device buffer
+                    (libsattn_probe.so) and prints one JSON line: the read
+                    bandwidth the split-KV decode is set against.
   --sq-summary D    reads a --pmc pass over the SQ counters listed in
                     SQ_COUNTERS (with --bench-log) and prints a markdown
                     summary (MFMA busy of the headline and every kernel).
@@ -537,6 +540,43 @@ def prefill_extra():
             "TFLOPs_graph": flops / tm["graph_us"]["median"] / 1e6,
             "TFLOPs_event": flops / tm["event_us"]["median"] / 1e6,
             "frac_of_bf16_peak": flops / tm["graph_us"]["median"] / 1e6 / PEAK_BF16_TFLOPS}
+
+
+def read_ceiling(gib=8, grids=(1024, 2048, 4096, 8192)):
+    """A bare streaming read of a resident ``gib`` GiB device buffer (the
+    probe library's 16-byte nontemporal loads, one contiguous slice per
+    workgroup), graph- and
+    event-timed like the extras: the bandwidth the split-KV decode is set
+    against. Nothing of the attention path runs here."""
+    import ctypes
+    import torch
+    from exact_tiled_attention_sattn_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit("%s is missing: build the package first" % PROBE_LIB)
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.sattn_probe_read.restype = ctypes.c_int
+    lib.sattn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
+    out = torch.empty(max(grids) * 256, dtype=torch.int32, device=DEV)
+    fns = {}
+    for g in grids:
+        def fn(g=g):
+            rc = lib.sattn_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                      out.numel(), g, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError("sattn_probe_read failed (%d)" % rc)
+        fns["grid %d" % g] = fn
+    t = time_variants(fns, seed=3)
+    res = {"workload": "streaming read of a resident %d GiB buffer, 16-byte nontemporal loads" % gib,
+           "bytes": nbytes, "timing": t}
+    res["GBps_graph"] = {n: nbytes / t[n]["graph_us"]["median"] / 1e3 for n in fns}
+    res["best_GBps_graph"] = max(res["GBps_graph"].values())
+    res["best_frac_of_hbm_peak"] = res["best_GBps_graph"] / PEAK_HBM_GBS
+    del buf, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def gqa_token_decode_extra():
@@ -1385,6 +1425,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-gate", action="store_true")
     ap.add_argument("--variants", action="store_true")
+    ap.add_argument("--read-ceiling", action="store_true")
     ap.add_argument("--trace-summary", metavar="DIR")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--sq-summary", metavar="DIR")
@@ -1410,6 +1451,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.read_ceiling:
+        print(json.dumps(read_ceiling()))
+        return
     from exact_tiled_attention_sattn_amd import sattn_fwd, library
     library()
 

@@ -24,6 +24,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsattn.so")
+# The bandwidth probe behind `bench.py --read-ceiling` (not part of the
+# attention path; its own library).
+PROBE_LIB = os.path.join(PKG, "libsattn_probe.so")
 UNITS = ["sattn", "k_fwd_dense", "k_fwd_varlen", "k_fwd_split", "k_fwd_cache", "k_fwd_sparse",
          "k_bwd_dense", "k_bwd_varlen", "k_bwd_sparse"]
 ARCH = "gfx950"
@@ -94,7 +97,7 @@ def build(verbose=False, variants=True, jobs=None):
     library path."""
     os.makedirs(OBJ, exist_ok=True)
     jobs = jobs or min(16, os.cpu_count() or 4)
-    tasks = [(u, "", []) for u in UNITS]
+    tasks = [(u, "", []) for u in UNITS] + [("probe_read", "", [])]
     if variants:
         tasks += [(u, "." + name, flags) for name, flags in VARIANTS.items() for u in VARIANT_UNITS]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -103,6 +106,7 @@ def build(verbose=False, variants=True, jobs=None):
         for f in cf.as_completed(futs):
             objs[futs[f]] = f.result()
     lib = _link([objs[(u, "")] for u in UNITS], LIB, verbose)
+    _link([objs[("probe_read", "")]], PROBE_LIB, verbose)
     if variants:
         for name in VARIANTS:
             parts = [objs[(u, "." + name)] if u in VARIANT_UNITS else objs[(u, "")] for u in UNITS]

@@ -387,3 +387,25 @@ def test_bwd_noalloc_zero_size_ok_without_pointers(lib):
     nulls = {x: 0 for x in BWD_PTRS}
     assert _bwd_noalloc(lib, n=0, **nulls) == 0
     assert _bwd_noalloc(lib, b=0, **nulls) == 0
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "sattn_probe.h")
+
+
+def test_probe_library_exports_its_header_and_rejects_bad_arguments(lib):
+    """The bandwidth probe (libsattn_probe.so, used by bench.py --read-ceiling)
+    exports what its header declares and refuses invalid calls before any
+    launch."""
+    from exact_tiled_attention_sattn_amd.build import PROBE_LIB
+    assert os.path.exists(PROBE_LIB), "libsattn_probe.so is built beside libsattn.so"
+    src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(sattn_[a-z_]+)\s*\(", src)))
+    assert names == ["sattn_probe_read"]
+    probe = ctypes.CDLL(PROBE_LIB)
+    probe.sattn_probe_read.restype = ctypes.c_int
+    probe.sattn_probe_read.argtypes = [ctypes.c_void_p, I64, ctypes.c_void_p, I64, ctypes.c_int, ctypes.c_void_p]
+    ok = dict(buf=FAKE, nbytes=1 << 20, out=FAKE2, count=1024 * 256, grid=1024)
+    for bad in (dict(buf=NULL), dict(out=NULL), dict(nbytes=0), dict(nbytes=100), dict(buf=ctypes.c_void_p(0x10008)),
+                dict(grid=0), dict(grid=70000), dict(count=1023 * 256)):
+        a = dict(ok, **bad)
+        assert probe.sattn_probe_read(a["buf"], a["nbytes"], a["out"], a["count"], a["grid"], NULL) == -1, bad

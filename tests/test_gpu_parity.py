@@ -1420,3 +1420,29 @@ def test_outputs_stay_in_bounds(dt, causal):
         assert _guards_intact(ob3, g3, o3.numel()) and _guards_intact(lb3, gl3, lse3.numel())
         o3_ref, lse3_ref = dense.attention_cache(W.to_f64(q3), W.to_f64(k3), W.to_f64(v3), sc3, causal)
         check_attention(o3.cpu(), lse3.cpu(), o3_ref, lse3_ref, dtype, "guards cache")
+
+
+@pytest.mark.parametrize("nbytes,grid", [(1 << 20, 64), ((1 << 20) + 48, 7), (4096, 1024)])
+def test_read_probe_reads_every_word_once(nbytes, grid):
+    """The streaming-read probe behind bench.py --read-ceiling: the XOR of
+    what its threads report equals the XOR of every 32-bit word of the
+    buffer (a word missed or read twice changes it), for ragged sizes and
+    more workgroups than 16-byte pieces."""
+    import ctypes
+    from exact_tiled_attention_sattn_amd.build import PROBE_LIB
+    _banner("read probe", nbytes, grid)
+    probe = ctypes.CDLL(PROBE_LIB)
+    probe.sattn_probe_read.restype = ctypes.c_int
+    probe.sattn_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_void_p]
+    g = torch.Generator().manual_seed(nbytes + grid)
+    words = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    buf = words.to(DEV)
+    out = torch.full((grid * 256,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    rc = probe.sattn_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()), out.numel(),
+                                grid, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(words.numpy().view(np.uint32))
+    assert got == want

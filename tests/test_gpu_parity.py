@@ -49,6 +49,8 @@ SMALL = [
     # many heads: D <= 64 problems that take the streaming kernel rather than
     # the small-problem kernel (more than 256 workgroups of 32 rows)
     (4, 16, 300, 64, "fp16"), (2, 40, 200, 32, "bf16"),
+    # ... and with long key walks (18 key tiles, ragged)
+    (2, 8, 1100, 64, "bf16"), (2, 8, 1100, 32, "fp16"),
 ]
 
 
